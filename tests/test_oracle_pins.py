@@ -1,0 +1,417 @@
+"""Pins for the CPU oracle, independent of the oracle's own code.
+
+Each test checks the oracle against something the pages or the mathematics
+fix: hand-worked quantization groups (re-derived here in exact rational
+arithmetic), packing patterns written by hand, brute-force vote counting,
+a stable sort, textbook attention (closed forms and torch's fp64 SDPA), and
+the KV-size statement on the MoQAE page (research background section).
+A final block plants plausible mistakes in copies of the quantizer and checks
+that the pins catch them.
+"""
+import itertools
+import json
+import math
+import os
+import struct
+from collections import Counter
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import mkv_oracle as orc
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+def fl32(x: Fraction) -> Fraction:
+    """Exact round-to-nearest-even of a rational to an IEEE float32 (normal
+    range only), written from the definition of the format."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert -126 <= e <= 127
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp
+    lo = math.floor(m)
+    rem = m - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * lo * ulp
+
+
+def rne_int(x: Fraction) -> int:
+    lo = math.floor(x)
+    rem = x - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return lo
+
+
+def f32_bits(v) -> int:
+    return struct.unpack("<I", struct.pack("<f", float(v)))[0]
+
+
+def exact_quantize(values, bits):
+    """The quantizer reading evaluated in exact rationals with explicit
+    float32 rounding at every operation (no numpy float32 involved)."""
+    L = (1 << bits) - 1
+    xs = [Fraction(float(v)) for v in values]
+    mn = min(xs)
+    mx = max(xs)
+    s = fl32(fl32(mx - mn) / L)
+    if s == 0:
+        return [0] * len(xs), s, mn
+    r = fl32(Fraction(1) / s)
+    codes = [min(max(rne_int(fl32(fl32(x - mn) * r)), 0), L) for x in xs]
+    return codes, s, mn
+
+
+def load_cases():
+    with open(os.path.join(GOLD, "quant_hand_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def case_group(c):
+    vals = list(c["head"]) + [c["fill"]] * (32 - len(c["head"]))
+    codes = list(c["codes_head"]) + [c["codes_fill"]] * (32 - len(c["head"]))
+    return np.array(vals, dtype=np.float16), codes
+
+
+def expected_s_bits(c):
+    return int(c["s_hex"], 16) if "s_hex" in c else f32_bits(c["s"])
+
+
+def expected_mn_bits(c):
+    return int(c["mn_hex"], 16) if "mn_hex" in c else f32_bits(c["mn"])
+
+
+# ---------------------------------------------------------------- quantizer pins
+@pytest.mark.parametrize("case", load_cases(), ids=lambda c: c["name"])
+def test_golden_fixture_is_self_consistent(case):
+    """The hand-worked fixture agrees with exact rational evaluation."""
+    g, codes = case_group(case)
+    ex_codes, ex_s, ex_mn = exact_quantize(g, case["bits"])
+    assert ex_codes == codes
+    assert f32_bits(float(ex_s)) == expected_s_bits(case)
+    assert f32_bits(float(ex_mn) + 0.0) == expected_mn_bits(case)
+    if "r_hex" in case:
+        assert f32_bits(float(fl32(1 / ex_s))) == int(case["r_hex"], 16)
+
+
+def check_quantizer_on_cases(qfun):
+    for case in load_cases():
+        g, codes = case_group(case)
+        q, s, mn = qfun(g[None, :], case["bits"])
+        assert q[0].tolist() == codes, case["name"]
+        assert f32_bits(s[0]) == expected_s_bits(case), case["name"]
+        assert f32_bits(mn[0]) == expected_mn_bits(case), case["name"]
+
+
+def test_oracle_quantizer_matches_hand_cases():
+    check_quantizer_on_cases(orc.quantize_groups)
+
+
+def test_dequant_round_trip_values():
+    # INT2 case 1: x_hat(0.5) = 1.0 exactly (error s/2, the bound is tight)
+    g = np.array([-1.0, 0.0, 0.5, 2.0] + [0.0] * 28, np.float16)
+    q, s, mn = orc.quantize_groups(g[None], 2)
+    xh = q[0].astype(np.float64) * float(s[0]) + float(mn[0])
+    assert xh[2] == 1.0 and abs(xh[2] - 0.5) == float(s[0]) / 2
+    # INT4 non-representable scale: x_hat(0.5) = 7 * fl32(1/15)
+    g = np.array([0.0, 1.0, 0.5, 0.25] + [0.0] * 28, np.float16)
+    q, s, mn = orc.quantize_groups(g[None], 4)
+    assert q[0, 2] * float(s[0]) + float(mn[0]) == pytest.approx(0.46666669100522995, abs=1e-15)
+    # constant group dequantizes exactly
+    g = np.full(32, 1.25, np.float16)
+    q, s, mn = orc.quantize_groups(g[None], 4)
+    assert np.all(q == 0) and float(s[0]) == 0.0 and float(mn[0]) == 1.25
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantizer_invariants_random(bits):
+    rng = np.random.default_rng(1234 + bits)
+    L = (1 << bits) - 1
+    for scale in (1.0, 8.0, 1e-3, 300.0):
+        g = (rng.standard_normal((4000, 32)) * scale).astype(np.float16)
+        q, s, mn = orc.quantize_groups(g, bits)
+        x = g.astype(np.float64)
+        xh = q.astype(np.float64) * s[:, None].astype(np.float64) + mn[:, None].astype(np.float64)
+        assert q.max() <= L
+        pos = s > 0
+        # the minimum maps to 0 and the maximum to L
+        amin = np.argmin(x, axis=1)
+        amax = np.argmax(x, axis=1)
+        rows = np.arange(len(x))
+        assert np.all(q[rows, amin][pos] == 0)
+        assert np.all(q[rows, amax][pos] == L)
+        # |x - x_hat| <= s/2 (+ a few float32 ulps of the range ends)
+        ulp = np.spacing(np.maximum(np.abs(x.min(1)), np.abs(x.max(1))).astype(np.float32)).astype(np.float64)
+        err = np.abs(x - xh).max(axis=1)
+        assert np.all(err <= s.astype(np.float64) / 2 + 4 * ulp)
+        # monotone: sorting x sorts the codes
+        o = np.argsort(x, axis=1, kind="stable")
+        qs = np.take_along_axis(q, o, axis=1)
+        assert np.all(np.diff(qs.astype(np.int32), axis=1) >= 0)
+        # exact agreement with rational evaluation on a sample
+        for i in range(0, 4000, 397):
+            ex_codes, ex_s, ex_mn = exact_quantize(g[i], bits)
+            assert q[i].tolist() == ex_codes
+            assert f32_bits(s[i]) == f32_bits(float(ex_s))
+
+
+def test_key_groups_run_along_tokens_value_groups_along_channels():
+    """Keys: one (scale, min) per (32-token group, channel); values: one per
+    (token, 32-channel group).  A chunk whose channel j spans [0, j+1] over
+    the tokens and whose token t spans [0, t+1] over the channels tells the
+    axes apart (KIVI note on the MoQAE page: keys per channel)."""
+    C, d = 64, 64
+    k = np.zeros((C, d), np.float16)
+    for j in range(d):
+        k[:, j] = np.float16((j % 16) + 1)
+        k[::32, j] = 0                                  # each 32-token group holds a 0
+    kq, ks, km = orc.quantize_chunk_k(k, 4)
+    assert ks.shape == (C // 32, d)
+    for j in range(d):
+        assert float(ks[0, j]) == np.float32(np.float32((j % 16) + 1) / np.float32(15))
+    v = np.zeros((C, d), np.float16)
+    for t in range(C):
+        v[t, :] = np.float16((t % 8) + 1)
+        v[t, ::32] = 0
+    vq, vs, vm = orc.quantize_chunk_v(v, 2)
+    assert vs.shape == (C, d // 32)
+    for t in range(C):
+        assert float(vs[t, 0]) == np.float32(np.float32((t % 8) + 1) / np.float32(3))
+
+
+# ---------------------------------------------------------------- packing pins
+def test_pack_words():
+    with open(os.path.join(GOLD, "pack_words.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        w = orc.pack_codes(np.array(c["codes"]), c["bits"])
+        assert [hex(int(x)) for x in w] == [h.lower() for h in c["words"]]
+        assert orc.unpack_codes(w, c["bits"]).tolist() == c["codes"]
+
+
+# ---------------------------------------------------------------- vote / RF / reorder pins
+def naive_vote(labels):
+    cnt = Counter(labels)
+    best = max(cnt.get(k, 0) for k in range(3))
+    return [k for k in range(3) if cnt.get(k, 0) == best][0]
+
+
+@pytest.mark.parametrize("C", [1, 2, 3, 5, 8])
+def test_vote_exhaustive_small_chunks(C):
+    labs = np.array(list(itertools.product(range(3), repeat=C)), dtype=np.uint8)
+    got = orc.chunk_vote(labs.reshape(1, -1), C, freeze_first=False)[0]
+    want = [naive_vote(list(r)) for r in labs]
+    assert got.tolist() == want
+
+
+def test_vote_crafted_counts_c32():
+    def chunk(c0, c1, c2):
+        return [0] * c0 + [1] * c1 + [2] * c2
+    e = np.array([chunk(11, 11, 10) + chunk(10, 11, 11) + chunk(10, 10, 12) + chunk(0, 16, 16)],
+                 dtype=np.uint8)
+    got = orc.chunk_vote(e, 32, freeze_first=False)[0].tolist()
+    assert got == [0, 1, 2, 1]
+
+
+def test_routing_freezing():
+    e = np.full((3, 4 * 32), 2, dtype=np.uint8)
+    with_rf = orc.bits_of(orc.chunk_vote(e, 32, freeze_first=True))
+    without = orc.bits_of(orc.chunk_vote(e, 32, freeze_first=False))
+    assert with_rf[:, 0].tolist() == [16, 16, 16] and np.all(with_rf[:, 1:] == 2)
+    assert np.all(without == 2)
+    # an appended batch starting at chunk 5 is never frozen
+    app = orc.chunk_vote(e, 32, freeze_first=True, chunk_offset=5)
+    assert np.all(app == 2)
+
+
+def test_reorder_is_stable_partition():
+    rng = np.random.default_rng(7)
+    v = rng.integers(0, 3, size=(6, 53)).astype(np.uint8)
+    perm, rank, seg = orc.reorder(v)
+    for b in range(6):
+        vb = v[b].tolist()
+        assert perm[b].tolist() == sorted(range(53), key=vb.__getitem__)
+        assert seg[b].tolist() == [vb.count(k) for k in range(3)]
+        for c in range(53):
+            assert rank[b, c] == sum(1 for c2 in range(c) if vb[c2] == vb[c])
+        # along perm the expert index never decreases; chunk index increases within a segment
+        ks = [vb[p] for p in perm[b]]
+        assert ks == sorted(ks)
+
+
+# ---------------------------------------------------------------- router pins
+def test_router_hand_identity_weights():
+    # D = 4, I = 2: W1 picks x0, x1; W2 picks x2, x3; u = (x0*x2, x1*x3)
+    x = np.array([[1.0, -2.0, 3.0, 0.5], [0.0, 1.0, -1.0, 4.0]])
+    w12 = np.array([[1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0], [0, 0, 0, 1]], dtype=np.float64)
+    w3 = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, -1.0]])
+    b3 = np.array([0.0, 0.25, -0.5])
+    z = orc.router_logits(x, w12, w3, b3, 2)
+
+    def silu(u):
+        return u / (1.0 + math.exp(-u))
+    for i, row in enumerate(x):
+        a0 = silu(row[0] * row[2])
+        a1 = silu(row[1] * row[3])
+        want = [a0 + b3[0], a1 + b3[1], a0 - a1 + b3[2]]
+        assert z[i].tolist() == pytest.approx(want, abs=1e-14)
+    assert orc.token_experts(z).tolist() == [int(np.argmax(z[0])), int(np.argmax(z[1]))]
+
+
+def test_router_brute_force_tiny():
+    rng = np.random.default_rng(3)
+    N, D, I = 5, 7, 3
+    x = rng.standard_normal((N, D))
+    w12 = rng.standard_normal((2 * I, D)) * 0.3
+    w3 = rng.standard_normal((3, I))
+    b3 = rng.standard_normal(3)
+    z = orc.router_logits(x, w12, w3, b3, I)
+    for n in range(N):
+        for k in range(3):
+            acc = []
+            for i in range(I):
+                h1 = math.fsum(x[n, j] * w12[i, j] for j in range(D))
+                h2 = math.fsum(x[n, j] * w12[I + i, j] for j in range(D))
+                u = h1 * h2
+                acc.append(w3[k, i] * u / (1.0 + math.exp(-u)))
+            assert z[n, k] == pytest.approx(math.fsum(acc) + b3[k], rel=1e-12, abs=1e-12)
+
+
+def test_token_expert_ties_go_to_lowest_index():
+    z = np.array([[1.0, 1.0, 0.0], [0.0, 2.0, 2.0], [3.0, 3.0, 3.0], [0.0, 0.0, 1.0]])
+    assert orc.token_experts(z).tolist() == [0, 1, 0, 2]
+
+
+def test_bf16_decode():
+    bits = np.array([0x3F80, 0xBFC0, 0x0000, 0x8000, 0x4049], dtype=np.uint16)
+    vals = orc.bf16_bits_to_f64(bits)
+    assert vals[:4].tolist() == [1.0, -1.5, 0.0, -0.0]
+    assert vals[4] == 3.140625
+
+
+# ---------------------------------------------------------------- attention pins
+def test_attention_closed_forms():
+    rng = np.random.default_rng(11)
+    T, d = 97, 64
+    k = rng.standard_normal((T, d))
+    v = rng.standard_normal((T, d))
+    # q = 0: uniform weights -> mean of the values
+    assert np.allclose(orc.attention(np.zeros(d), k, v), v.mean(0), atol=1e-13)
+    # one-hot query: q = lam * k_t* dominates -> v_t*
+    t = 41
+    o = orc.attention(200.0 * k[t] / np.linalg.norm(k[t]) * math.sqrt(d), k, v)
+    assert np.allclose(o, v[t], atol=1e-9)
+    # permuting keys and values together changes nothing
+    q = rng.standard_normal(d)
+    p = rng.permutation(T)
+    assert np.allclose(orc.attention(q, k[p], v[p]), orc.attention(q, k, v), atol=1e-12)
+
+
+def test_attention_brute_force_and_sdpa():
+    import torch
+    rng = np.random.default_rng(12)
+    T, d = 19, 8
+    q = rng.standard_normal(d)
+    k = rng.standard_normal((T, d))
+    v = rng.standard_normal((T, d))
+    o = orc.attention(q, k, v)
+    sc = [math.fsum(q[j] * k[t, j] for j in range(d)) / math.sqrt(d) for t in range(T)]
+    m = max(sc)
+    w = [math.exp(s - m) for s in sc]
+    Z = math.fsum(w)
+    want = [math.fsum(w[t] * v[t, j] for t in range(T)) / Z for j in range(d)]
+    assert np.allclose(o, want, atol=1e-13)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, None], torch.from_numpy(k)[None, None],
+        torch.from_numpy(v)[None, None])[0, 0, 0].numpy()
+    assert np.allclose(o, ref, atol=1e-12)
+
+
+def test_all_fp16_chunks_equal_plain_attention():
+    """With every chunk FP16 the dequantized cache is the fp16 cache itself."""
+    rng = np.random.default_rng(13)
+    C, d = 64, 64
+    k = rng.standard_normal((2 * C, d)).astype(np.float16)
+    v = rng.standard_normal((2 * C, d)).astype(np.float16)
+    q = rng.standard_normal(d).astype(np.float16)
+    parts = [orc.dequant_chunk(orc.quantize_chunk(k[i * C:(i + 1) * C], v[i * C:(i + 1) * C], 16))
+             for i in range(2)]
+    kh = np.concatenate([p[0] for p in parts])
+    vh = np.concatenate([p[1] for p in parts])
+    assert np.array_equal(kh, k.astype(np.float64))
+    o = orc.attention(q, kh, vh)
+    import torch
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[None, None, None],
+        torch.from_numpy(k.astype(np.float64))[None, None],
+        torch.from_numpy(v.astype(np.float64))[None, None])[0, 0, 0].numpy()
+    assert np.allclose(o, ref, atol=1e-12)
+
+
+def test_kv_size_statement_moqae_background():
+    """MoQAE notes, research background: the FP16 KV cache of Llama2-13B at
+    128k context reaches about 100 GB.  2 (K,V) x 40 layers x 40 heads x 128
+    x 2 bytes x 131072 tokens = 107.4e9 bytes."""
+    from chunk_mixed_precision_amd import configs
+    assert configs.fp16_kv_bytes(layers=40, heads=40, head_dim=128, tokens=131072) == 107374182400
+    assert 95e9 < 107374182400 < 115e9
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _quant_variant(mistake):
+    def q(g, bits):
+        L = np.float32((1 << bits) - 1)
+        x = np.asarray(g).astype(np.float32)
+        mn = x.min(axis=-1)
+        mx = x.max(axis=-1)
+        if mistake != "no_zero_canon":
+            mn = (mn + np.float32(0.0)).astype(np.float32)
+        s = ((mx - mn).astype(np.float32) / L).astype(np.float32)
+        zero = s == 0
+        safe = np.where(zero, np.float32(1.0), s).astype(np.float32)
+        r = (np.float32(1.0) / safe).astype(np.float32)
+        t = (x - mn[..., None]).astype(np.float32)
+        if mistake == "divide":
+            t = (t / safe[..., None]).astype(np.float32)
+        else:
+            t = (t * r[..., None]).astype(np.float32)
+        if mistake == "half_away":
+            qv = np.floor(t + np.float32(0.5))
+        elif mistake == "truncate":
+            qv = np.floor(t)
+        else:
+            qv = np.rint(t)
+        if mistake == "bad_levels":
+            qv = np.clip(qv, 0, L - 1)
+        else:
+            qv = np.clip(qv, 0, L)
+        qv[zero] = 0
+        return qv.astype(np.uint8), s, mn
+    return q
+
+
+@pytest.mark.parametrize("mistake", ["divide", "half_away", "truncate", "no_zero_canon", "bad_levels"])
+def test_pins_catch_planted_quantizer_mistakes(mistake):
+    with pytest.raises(AssertionError):
+        check_quantizer_on_cases(_quant_variant(mistake))
+
+
+def test_pins_catch_vote_tie_mistake():
+    # a vote that breaks ties toward the lower-precision expert disagrees
+    labs = np.array([[0, 2], [1, 2]], dtype=np.uint8)
+    ok = orc.chunk_vote(labs.reshape(1, -1), 2, freeze_first=False)[0].tolist()
+    assert ok == [0, 1]
+    wrong = [max(set(r.tolist()), key=lambda k: (r.tolist().count(k), k)) for r in labs]
+    assert wrong != ok
