@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Throughput of the chunk-adaptive mixed-precision KV path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+of the named workload:
+  route   mkv_route_chunks       router GEMM (bf16 MFMA) -> vote -> freezing -> reorder
+  pack    mkv_quantize_pack_kv   K/V of every chunk -> packed FP16/INT4/INT2 segments
+  attend  mkv_mixed_kv_decode_attention   one decode query per (sequence, head)
+
+Inputs are resident in HBM before timing starts.  The packed cache is kept
+in R copies (R >= 4, >= 1 GiB in total): step i packs into copy i % R and
+attends over copy (i + 1) % R, whose bytes are identical (same inputs, same
+deterministic kernels) and were written R - 1 steps earlier, so the 256 MB
+last-level cache cannot serve the attention read.
+
+Prints one JSON line.  value = decode-attention effective GB/s (packed KV
+bytes + q + out per launch / attention time); the quantize rate, router rate
+and per-kernel times are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def parse():
+    from chunk_mixed_precision_amd import configs
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=configs.LLAMA2_7B_32K.name, choices=[w.name for w in configs.ALL])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the oracle timing on the host (0 disables it)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, k, v, q, tab_bits, budget_s):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload:
+    whole (sequence 0, KV head h) slices, quantized then attended, one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from chunk_mixed_precision_amd import configs
+    from oracle import mkv_oracle as orc
+
+    bits_row = tab_bits[0]
+    g = w.Hq // w.Hkv
+    t_quant = t_attn = 0.0
+    nbytes = 0
+    heads = 0
+    tokens = 0
+    with threadpool_limits(limits=1):
+        for h in range(w.Hkv):
+            kk = k[0, h].cpu().numpy()
+            vv = v[0, h].cpu().numpy()
+            qq = q[0, h * g:(h + 1) * g].cpu().numpy()
+            t0 = time.perf_counter()
+            chunks = [orc.quantize_chunk(kk[c * w.C:(c + 1) * w.C], vv[c * w.C:(c + 1) * w.C], int(bits_row[c]))
+                      for c in range(w.n)]
+            t1 = time.perf_counter()
+            deq = [orc.dequant_chunk(ch) for ch in chunks]
+            kh = np.concatenate([d[0] for d in deq])
+            vh = np.concatenate([d[1] for d in deq])
+            for j in range(g):
+                orc.attention(qq[j].astype(np.float64), kh, vh)
+            t2 = time.perf_counter()
+            t_quant += t1 - t0
+            t_attn += t2 - t1
+            nbytes += sum(configs.chunk_bytes(int(b), w.d, w.C) for b in bits_row[:w.n]) + g * w.d * 6
+            tokens += w.T
+            heads += 1
+            if t_quant + t_attn >= budget_s:
+                break
+    return {
+        "value": round(nbytes / t_attn / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"sequence 0, {heads} of {w.Hkv} KV heads of {w.name}: oracle dequant + fp64 attention "
+                   f"over {w.T} tokens per head ({t_attn:.1f} s); oracle quantize of the same slices "
+                   f"{tokens / t_quant:.0f} tokens/s per head-slice ({t_quant:.1f} s); numpy, 1 thread"),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(pass --gpus 1; sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from chunk_mixed_precision_amd import configs, mkv, synth
+
+    w = configs.BY_NAME[args.workload]
+    if not w.routed or w.append_chunks or w.layers != 1:
+        print(f"bench.py times the single-layer routed workloads; {w.name} is a parity-test case",
+              file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    mkv.lib()
+
+    # ---------------- inputs, resident in HBM
+    x, w12, w3, b3 = synth.router_inputs(w)
+    x, w12, w3, b3 = x.to(dev), w12.to(dev), w3.to(dev), b3.to(dev)
+    k, v = synth.kv(w, dev)
+    q = synth.query(w, dev)
+    tab = mkv.RouteTables(w.B, w.n, dev)
+    ws_route = torch.empty(mkv.workspace_bytes_route(w.B, w.T, w.D, w.I), dtype=torch.uint8, device=dev)
+    mkv.route_chunks(tab, w.C, x=x, w12=w12, w3=w3, b3=b3, workspace=ws_route)
+    torch.cuda.synchronize()
+    seg = tab.seg_count.cpu().numpy()
+    caps = [int(seg[:, kk].max()) for kk in range(3)]
+    one = mkv.PackedCache(w.B, w.Hkv, w.d, w.C, caps, tab.seg_count, dev)
+    cache_bytes = one.nbytes()
+    R = max(4, math.ceil((1 << 30) / cache_bytes))
+    caches = [one] + [mkv.PackedCache(w.B, w.Hkv, w.d, w.C, caps, tab.seg_count, dev) for _ in range(R - 1)]
+    for c in caches:
+        mkv.quantize_pack_kv(k, v, tab, c)
+    ws_attn = torch.empty(mkv.workspace_bytes_attention(w.B, w.Hq, w.Hkv, w.d, w.C, caps), dtype=torch.uint8,
+                          device=dev)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    nev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nev)]
+
+    def step(i, rec):
+        e = ev[i] if rec else None
+        if e:
+            e[0].record()
+        mkv.route_chunks(tab, w.C, x=x, w12=w12, w3=w3, b3=b3, workspace=ws_route)
+        if e:
+            e[1].record()
+        mkv.quantize_pack_kv(k, v, tab, caches[i % R])
+        if e:
+            e[2].record()
+        mkv.mixed_kv_decode_attention(q, caches[(i + 1) % R], out=out, workspace=ws_attn)
+        if e:
+            e[3].record()
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_route = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
+    t_pack = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
+    t_attn = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(nev)]) * 1e-3
+
+    attn_bytes = configs.effective_attention_bytes(w, seg)
+    pack_read = w.B * w.Hkv * w.T * w.d * 2 * 2
+    pack_write = sum(int(seg[b, kk]) * configs.chunk_bytes(bits, w.d, w.C) * w.Hkv
+                     for b in range(w.B) for kk, bits in enumerate(configs.EXPERT_BITS))
+    router_flop = 2.0 * w.B * w.T * w.D * 2 * w.I + 2.0 * w.B * w.T * w.I * 3
+    a_mean = float(t_attn.mean())
+    attn_gbs = attn_bytes / a_mean / 1e9
+    avg_bits = float(sum(seg[:, kk].sum() * bits for kk, bits in enumerate(configs.EXPERT_BITS)) / seg.sum())
+
+    res = {
+        "metric": "mixed-KV decode attention effective HBM GB/s (+ quantize tokens/s)",
+        "value": round(attn_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded), random-init router",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "context": w.T, "chunk": w.C, "router_hidden": w.D, "router_inner": w.I,
+                   "chunk_mix": [int(s) for s in seg.sum(0)], "avg_bits": round(avg_bits, 3),
+                   "cache_copies": R},
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attention (tile + combine launches of one call)",
+                     "bytes_per_launch": attn_bytes, "avg_launch_us": round(a_mean * 1e6, 3)},
+        "quantize_tokens_per_s": round(w.B * w.T / float(t_pack.mean()), 1),
+        "kernels": {
+            "route": {"us": round(float(t_route.mean()) * 1e6, 2),
+                      "tflops": round(router_flop / float(t_route.mean()) / 1e12, 2),
+                      "frac_bf16_peak": round(router_flop / float(t_route.mean()) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+            "pack": {"us": round(float(t_pack.mean()) * 1e6, 2),
+                     "gbs": round((pack_read + pack_write) / float(t_pack.mean()) / 1e9, 2),
+                     "frac_hbm": round((pack_read + pack_write) / float(t_pack.mean()) / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes": pack_read + pack_write},
+            "attend": {"us": round(a_mean * 1e6, 2), "us_p10": round(float(np.percentile(t_attn, 10)) * 1e6, 2),
+                       "us_p90": round(float(np.percentile(t_attn, 90)) * 1e6, 2), "bytes": attn_bytes},
+        },
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, k, v, q, tab.chunk_bits.cpu().numpy(), args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

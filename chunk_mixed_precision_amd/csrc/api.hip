@@ -1,0 +1,219 @@
+// C ABI of libmkv.so: argument checks, workspace sizing and launches.
+// Nothing here allocates device memory or keeps state between calls; every
+// argument error is reported before the first launch.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mkv.h"
+#include "mkv_internal.h"
+#include "mkv_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MKV_OK;
+    g_last_hip = (int)e;
+    return MKV_ERR_HIP;
+}
+
+// Groups per attention tile in each pool (FP16, INT4, INT2).  Tiles of one
+// bitwidth carry a similar number of bytes: 64 KB (FP16), 48 KB (INT4) and
+// 64 KB (INT2) at d = 128.
+inline void attn_tiles(int d, const int* cap, int C, int tg[3], int nt[3], int& nt_total) {
+    const int base[3] = {4, 8, 16};
+    nt_total = 0;
+    for (int k = 0; k < 3; ++k) {
+        tg[k] = d == 64 ? 2 * base[k] : base[k];
+        const long groups = (long)cap[k] * (C / mkv::kGroup);
+        nt[k] = (int)((groups + tg[k] - 1) / tg[k]);
+        nt_total += nt[k];
+    }
+}
+
+inline bool valid_cache(const mkv_cache* c) {
+    if (!c) return false;
+    if (c->B <= 0 || c->Hkv <= 0 || c->C <= 0 || c->d <= 0) return false;
+    for (int k = 0; k < 3; ++k) {
+        if (c->cap[k] < 0) return false;
+        if (c->cap[k] > 0 && (!c->pool[k] || !aligned16(c->pool[k]))) return false;
+    }
+    if (!c->seg_count) return false;
+    return true;
+}
+
+inline int check_cache_shape(const mkv_cache* c) {
+    if (c->d != 64 && c->d != 128) return MKV_ERR_UNSUPPORTED;
+    if (c->C % 32 != 0 || c->C < 32 || c->C > 1024) return MKV_ERR_UNSUPPORTED;
+    if ((long)c->B * c->Hkv > 65535) return MKV_ERR_UNSUPPORTED;
+    return MKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mkv_version(void) { return 1; }
+
+int mkv_last_hip_error(void) { return g_last_hip; }
+
+const char* mkv_status_string(int status) {
+    switch (status) {
+        case MKV_OK: return "ok";
+        case MKV_ERR_ARG: return "invalid argument (null pointer, bad size or misaligned buffer)";
+        case MKV_ERR_UNSUPPORTED: return "shape not supported by the kernels";
+        case MKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case MKV_ERR_HIP: return "HIP runtime error (see mkv_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+size_t mkv_group_bytes(int bits, int d) {
+    if ((bits != 16 && bits != 4 && bits != 2) || (d != 64 && d != 128)) return 0;
+    return mkv::group_bytes(bits, d);
+}
+
+size_t mkv_pool_bytes(int bits, int B, int Hkv, int cap, int d, int C) {
+    const size_t gb = mkv_group_bytes(bits, d);
+    if (!gb || B < 0 || Hkv < 0 || cap < 0 || C <= 0 || C % 32) return 0;
+    return (size_t)B * Hkv * cap * (C / 32) * gb;
+}
+
+size_t mkv_workspace_bytes(int op, int a, int b, int c, int e, int f, const int* caps) {
+    if (op == MKV_OP_ROUTE) {
+        const int B = a, T = b, I = e;
+        if (B <= 0 || T <= 0 || I <= 0 || I % mkv::kRouterBI) return 0;
+        return (size_t)(I / mkv::kRouterBI) * B * T * 3 * sizeof(float);
+    }
+    if (op == MKV_OP_ATTENTION) {
+        const int B = a, Hq = b, Hkv = c, d = e, C = f;
+        if (!caps || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (d != 64 && d != 128) || C <= 0 || C % 32) return 0;
+        int tg[3], nt[3], ntt;
+        attn_tiles(d, caps, C, tg, nt, ntt);
+        return (size_t)B * Hkv * ntt * (Hq / Hkv) * (d + 4) * sizeof(float) + 16;
+    }
+    return 0;
+}
+
+int mkv_route_chunks(const void* x_bf16, const void* w12_bf16, const float* w3, const float* b3,
+                     float* logits, int B, int T, int D, int I, int C, unsigned flags,
+                     uint8_t* token_expert, const mkv_tables* tab, int chunk_offset,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    const bool logits_in = (flags & MKV_LOGITS_IN) != 0;
+    const bool append = (flags & MKV_APPEND) != 0;
+    if (flags & ~(MKV_FREEZE_FIRST | MKV_LOGITS_IN | MKV_APPEND)) return MKV_ERR_ARG;
+    if (!tab || !tab->chunk_bits || !tab->chunk_rank || !tab->perm || !tab->seg_count) return MKV_ERR_ARG;
+    if (B <= 0 || T <= 0 || C <= 0) return MKV_ERR_ARG;
+    if (C % 32 != 0 || C > 1024 || T % C != 0) return MKV_ERR_UNSUPPORTED;
+    if (chunk_offset < 0 || (!append && chunk_offset != 0)) return MKV_ERR_ARG;
+    const int n_new = T / C;
+    if (tab->n_max <= 0 || chunk_offset + n_new > tab->n_max) return MKV_ERR_ARG;
+    if (B > 65535 || n_new > 2147483647 / 1) return MKV_ERR_UNSUPPORTED;
+    if (logits_in) {
+        if (!logits || !aligned16(logits)) return MKV_ERR_ARG;
+    } else {
+        if (!x_bf16 || !w12_bf16 || !w3 || !b3) return MKV_ERR_ARG;
+        if (!aligned16(x_bf16) || !aligned16(w12_bf16) || !aligned16(w3)) return MKV_ERR_ARG;
+        if (logits && !aligned16(logits)) return MKV_ERR_ARG;
+        if (D <= 0 || I <= 0) return MKV_ERR_ARG;
+        if (D % 64 != 0 || I % mkv::kRouterBI != 0) return MKV_ERR_UNSUPPORTED;
+        const size_t need = mkv_workspace_bytes(MKV_OP_ROUTE, B, T, D, I, 0, nullptr);
+        if (!workspace || !aligned16(workspace) || workspace_bytes < need) return MKV_ERR_WORKSPACE;
+        if ((long)B * T > 2147483647L) return MKV_ERR_UNSUPPORTED;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const int M = B * T;
+    if (!logits_in) {
+        mkv::RouterParams rp{static_cast<const uint16_t*>(x_bf16), static_cast<const uint16_t*>(w12_bf16), w3,
+                             static_cast<float*>(workspace), M, D, I};
+        int s = hip_status(mkv::launch_router(rp, st));
+        if (s) return s;
+    }
+    mkv::VoteParams vp{};
+    vp.zpart = logits_in ? nullptr : static_cast<const float*>(workspace);
+    vp.ntile = logits_in ? 0 : I / mkv::kRouterBI;
+    vp.b3 = b3;
+    vp.logits_in = logits_in ? logits : nullptr;
+    vp.logits_out = logits_in ? nullptr : logits;
+    vp.token_expert = token_expert;
+    vp.chunk_bits = tab->chunk_bits;
+    vp.B = B; vp.T = T; vp.C = C; vp.n_max = tab->n_max; vp.chunk_offset = chunk_offset;
+    vp.freeze_first = (flags & MKV_FREEZE_FIRST) ? 1 : 0;
+    int s = hip_status(mkv::launch_vote(vp, n_new, st));
+    if (s) return s;
+    mkv::ReorderParams op{tab->chunk_bits, tab->chunk_rank, tab->perm, tab->seg_count,
+                          chunk_offset + n_new, tab->n_max, nullptr};
+    return hip_status(mkv::launch_reorder(op, B, st));
+}
+
+int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T, int chunk_offset,
+                         const mkv_tables* tab, const mkv_cache* cache, void* stream) {
+    if (!k_fp16 || !v_fp16 || !aligned16(k_fp16) || !aligned16(v_fp16)) return MKV_ERR_ARG;
+    if (!tab || !tab->chunk_bits || !tab->chunk_rank) return MKV_ERR_ARG;
+    if (!valid_cache(cache)) return MKV_ERR_ARG;
+    int s = check_cache_shape(cache);
+    if (s) return s;
+    if (T <= 0 || T % cache->C != 0) return MKV_ERR_ARG;
+    if (chunk_offset < 0 || chunk_offset + T / cache->C > tab->n_max) return MKV_ERR_ARG;
+    if ((long)T / 32 > 2147483647L) return MKV_ERR_UNSUPPORTED;
+    mkv::QuantParams qp{};
+    qp.k = static_cast<const uint16_t*>(k_fp16);
+    qp.v = static_cast<const uint16_t*>(v_fp16);
+    qp.B = cache->B; qp.Hkv = cache->Hkv; qp.T = T; qp.C = cache->C;
+    qp.chunk_offset = chunk_offset; qp.n_max = tab->n_max;
+    qp.chunk_bits = tab->chunk_bits; qp.chunk_rank = tab->chunk_rank;
+    for (int k = 0; k < 3; ++k) {
+        qp.cap[k] = cache->cap[k];
+        qp.pool[k] = static_cast<uint8_t*>(cache->pool[k]);
+    }
+    qp.overflow = cache->overflow;
+    return hip_status(mkv::launch_quant(qp, cache->d, T / 32, (hipStream_t)stream));
+}
+
+int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq, const mkv_cache* cache,
+                                  const void* tail_k_fp16, const void* tail_v_fp16, int tail_len,
+                                  float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q_fp16 || !out || !aligned16(q_fp16) || !aligned16(out)) return MKV_ERR_ARG;
+    if (!valid_cache(cache)) return MKV_ERR_ARG;
+    int s = check_cache_shape(cache);
+    if (s) return s;
+    if (Hq <= 0 || Hq % cache->Hkv != 0) return MKV_ERR_ARG;
+    const int g = Hq / cache->Hkv;
+    if (g != 1 && g != 2 && g != 4) return MKV_ERR_UNSUPPORTED;
+    if ((long)cache->B * Hq > 2147483647L) return MKV_ERR_UNSUPPORTED;
+    if (tail_len < 0 || tail_len >= 4096) return MKV_ERR_ARG;
+    if (tail_len > 0 && (!tail_k_fp16 || !tail_v_fp16)) return MKV_ERR_ARG;
+    const size_t need = mkv_workspace_bytes(MKV_OP_ATTENTION, cache->B, Hq, cache->Hkv, cache->d, cache->C, cache->cap);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return MKV_ERR_WORKSPACE;
+
+    mkv::AttnParams ap{};
+    ap.q = static_cast<const uint16_t*>(q_fp16);
+    for (int k = 0; k < 3; ++k) {
+        ap.pool[k] = static_cast<const uint8_t*>(cache->pool[k]);
+        ap.cap[k] = cache->cap[k];
+    }
+    ap.seg_count = cache->seg_count;
+    ap.B = cache->B; ap.Hkv = cache->Hkv; ap.Hq = Hq; ap.C = cache->C;
+    attn_tiles(cache->d, cache->cap, cache->C, ap.tg, ap.nt, ap.nt_total);
+    ap.part = static_cast<float*>(workspace);
+    ap.qscale = (float)(1.4426950408889634 / sqrt((double)cache->d));
+
+    mkv::CombineParams cp{};
+    cp.part = ap.part;
+    cp.seg_count = cache->seg_count;
+    cp.q = ap.q;
+    cp.tail_k = static_cast<const uint16_t*>(tail_k_fp16);
+    cp.tail_v = static_cast<const uint16_t*>(tail_v_fp16);
+    cp.tail_len = tail_len;
+    cp.out = out;
+    cp.B = cache->B; cp.Hkv = cache->Hkv; cp.Hq = Hq; cp.C = cache->C;
+    for (int k = 0; k < 3; ++k) { cp.cap[k] = ap.cap[k]; cp.tg[k] = ap.tg[k]; cp.nt[k] = ap.nt[k]; }
+    cp.nt_total = ap.nt_total;
+    cp.qscale = ap.qscale;
+    return hip_status(mkv::launch_attention(ap, cp, cache->d, g, (hipStream_t)stream));
+}
+
+}  // extern "C"

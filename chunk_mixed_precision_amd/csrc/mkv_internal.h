@@ -1,0 +1,50 @@
+// Internal definitions shared by the kernels of libmkv.so (not part of the
+// C ABI).  The packed-cache layout documented in include/mkv.h is expressed
+// here once, as index functions used by both the writer (quantize/pack) and
+// the reader (decode attention).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mkv {
+
+constexpr int kGroup = 32;   // tokens per group block / values per quant group
+
+// Expert index <-> bitwidth.
+__host__ __device__ constexpr int bits_of_expert(int k) { return k == 0 ? 16 : (k == 1 ? 4 : 2); }
+__host__ __device__ constexpr int expert_of_bits(int b) { return b == 16 ? 0 : (b == 4 ? 1 : (b == 2 ? 2 : -1)); }
+
+// Rows (of S 16-byte cells) in each section of a group block.
+__host__ __device__ constexpr int kc_rows(int bits) { return bits == 16 ? 32 : 2 * bits; }
+__host__ __device__ constexpr int km_rows(int bits) { return bits == 16 ? 0 : 4; }
+__host__ __device__ constexpr int vc_rows(int bits) { return bits == 16 ? 32 : 2 * bits; }
+__host__ __device__ constexpr int vm_rows(int bits) { return bits == 16 ? 0 : 4; }
+__host__ __device__ constexpr int group_rows(int bits) {
+    return kc_rows(bits) + km_rows(bits) + vc_rows(bits) + vm_rows(bits);
+}
+// Row offsets of the sections.
+__host__ __device__ constexpr int km_row0(int bits) { return kc_rows(bits); }
+__host__ __device__ constexpr int vc_row0(int bits) { return kc_rows(bits) + km_rows(bits); }
+__host__ __device__ constexpr int vm_row0(int bits) { return kc_rows(bits) + km_rows(bits) + vc_rows(bits); }
+
+__host__ __device__ constexpr int lane_slots(int d) { return d / 8; }
+__host__ __device__ constexpr size_t group_bytes(int bits, int d) {
+    return (size_t)group_rows(bits) * lane_slots(d) * 16;
+}
+
+// Token permutation of the key rows/fields of lane slot L (S = d/8 slots).
+// Field position r of lane slot L holds token r ^ tok_xor(S, L).  The xor
+// masks make the reduce-scatter of the q.k partial sums over the S lanes of
+// a row select-free: at each butterfly step every lane keeps the low half of
+// its registers and its partner's high half holds the same tokens.
+__host__ __device__ constexpr int tok_xor(int S, int L) {
+    return S == 16 ? ((((L >> 3) & 1) * 24) ^ (((L >> 2) & 1) * 14) ^ (((L >> 1) & 1) * 4) ^ ((L & 1) * 2))
+                   : ((((L >> 2) & 1) * 28) ^ (((L >> 1) & 1) * 8) ^ ((L & 1) * 4));
+}
+
+// Values: lane slot L covers value group G = L % NG and tokens tq + 4m,
+// tq = L / NG, m = 0..7 (NG = d/32).
+__host__ __device__ constexpr int vslot_of(int tq, int G, int NG) { return tq * NG + G; }
+
+}  // namespace mkv

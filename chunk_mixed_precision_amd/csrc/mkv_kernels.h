@@ -1,0 +1,91 @@
+// Kernel parameter blocks and kernel declarations of libmkv.so (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+namespace mkv {
+
+// ---------------------------------------------------------------- router
+constexpr int kRouterBM = 128;   // tokens per workgroup tile
+constexpr int kRouterBI = 64;    // inner indices per workgroup tile (64 W1 + 64 W2 rows)
+constexpr int kRouterBK = 32;    // K step staged in LDS
+
+struct RouterParams {
+    const uint16_t* x;      // [M][D] bf16 bits
+    const uint16_t* w12;    // [2I][D] bf16 bits
+    const float* w3;        // [3][I]
+    float* zpart;           // [I/kRouterBI][M][3] partial logits
+    int M, D, I;
+};
+
+struct VoteParams {
+    const float* zpart;     // router mode: [ntile][M][3]; NULL in logits-in mode
+    int ntile;
+    const float* b3;        // [3] (router mode)
+    const float* logits_in; // logits-in mode: [B][T][3]
+    float* logits_out;      // router mode, optional
+    uint8_t* token_expert;  // optional [B][T]
+    uint8_t* chunk_bits;    // [B][n_max]
+    int B, T, C, n_max, chunk_offset;
+    int freeze_first;
+};
+
+struct ReorderParams {
+    const uint8_t* chunk_bits;
+    int32_t* chunk_rank;
+    int32_t* perm;
+    int32_t* seg_count;
+    int n_total, n_max;
+    int32_t* bad;           // optional: set when a chunk's bitwidth is invalid
+};
+
+// ---------------------------------------------------------------- quantize
+struct QuantParams {
+    const uint16_t* k;      // [B][Hkv][T][d] fp16 bits
+    const uint16_t* v;
+    int B, Hkv, T, C, chunk_offset, n_max;
+    const uint8_t* chunk_bits;
+    const int32_t* chunk_rank;
+    int cap[3];
+    uint8_t* pool[3];
+    int32_t* overflow;
+};
+
+// ---------------------------------------------------------------- attention
+struct AttnParams {
+    const uint16_t* q;      // [B][Hq][d]
+    const uint8_t* pool[3];
+    int cap[3];
+    const int32_t* seg_count;
+    int B, Hkv, Hq, C;
+    int tg[3];              // groups per tile in each pool
+    int nt[3];              // tiles per (b, h) in each pool (at capacity)
+    int nt_total;
+    float* part;            // [B*Hkv][nt_total][g][d+2]: o[d], m (log2 domain), l
+    float qscale;           // log2(e) / sqrt(d)
+};
+
+struct CombineParams {
+    const float* part;
+    const int32_t* seg_count;
+    const uint16_t* q;
+    const uint16_t* tail_k; // [B][Hkv][tail_len][d]
+    const uint16_t* tail_v;
+    int tail_len;
+    float* out;             // [B][Hq][d]
+    int B, Hkv, Hq, C;
+    int cap[3];
+    int tg[3], nt[3], nt_total;
+    float qscale;
+};
+
+// Host-side launchers (each defined next to its kernels).
+hipError_t launch_router(const RouterParams& rp, hipStream_t st);
+hipError_t launch_vote(const VoteParams& vp, int n_new, hipStream_t st);
+hipError_t launch_reorder(const ReorderParams& rp, int B, hipStream_t st);
+hipError_t launch_quant(const QuantParams& qp, int D, int ngroups, hipStream_t st);
+hipError_t launch_attention(const AttnParams& ap, const CombineParams& cp, int D, int HB, hipStream_t st);
+
+}  // namespace mkv

@@ -1,0 +1,229 @@
+"""ctypes binding over libmkv.so (C ABI in include/mkv.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+Tensors are torch tensors on the GPU; their data pointers and the current
+torch stream are handed to the library as plain pointers.  If the library
+is not built, the first call raises (there is no CPU fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+from .configs import EXPERT_BITS, GROUP
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmkv.so")
+
+MKV_OK = 0
+MKV_ERR_ARG = -1
+MKV_ERR_UNSUPPORTED = -2
+MKV_ERR_WORKSPACE = -3
+MKV_ERR_HIP = -4
+
+MKV_FREEZE_FIRST = 0x1
+MKV_LOGITS_IN = 0x2
+MKV_APPEND = 0x4
+
+MKV_OP_ROUTE = 1
+MKV_OP_ATTENTION = 2
+
+EXPORTED = (
+    "mkv_route_chunks", "mkv_quantize_pack_kv", "mkv_mixed_kv_decode_attention",
+    "mkv_workspace_bytes", "mkv_group_bytes", "mkv_pool_bytes",
+    "mkv_status_string", "mkv_last_hip_error", "mkv_version",
+)
+
+
+class MkvTables(ctypes.Structure):
+    _fields_ = [("chunk_bits", ctypes.c_void_p), ("chunk_rank", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p), ("seg_count", ctypes.c_void_p),
+                ("n_max", ctypes.c_int)]
+
+
+class MkvCache(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("Hkv", ctypes.c_int), ("d", ctypes.c_int), ("C", ctypes.c_int),
+                ("cap", ctypes.c_int * 3), ("pool", ctypes.c_void_p * 3),
+                ("seg_count", ctypes.c_void_p), ("overflow", ctypes.c_void_p)]
+
+
+class MkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Open libmkv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m chunk_mixed_precision_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, u, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+        L.mkv_route_chunks.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, u, vp,
+                                       ctypes.POINTER(MkvTables), i, vp, sz, vp]
+        L.mkv_route_chunks.restype = i
+        L.mkv_quantize_pack_kv.argtypes = [vp, vp, i, i, ctypes.POINTER(MkvTables),
+                                           ctypes.POINTER(MkvCache), vp]
+        L.mkv_quantize_pack_kv.restype = i
+        L.mkv_mixed_kv_decode_attention.argtypes = [vp, i, ctypes.POINTER(MkvCache), vp, vp, i,
+                                                    vp, vp, sz, vp]
+        L.mkv_mixed_kv_decode_attention.restype = i
+        L.mkv_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int)]
+        L.mkv_workspace_bytes.restype = sz
+        L.mkv_group_bytes.argtypes = [i, i]
+        L.mkv_group_bytes.restype = sz
+        L.mkv_pool_bytes.argtypes = [i, i, i, i, i, i]
+        L.mkv_pool_bytes.restype = sz
+        L.mkv_status_string.argtypes = [i]
+        L.mkv_status_string.restype = ctypes.c_char_p
+        L.mkv_last_hip_error.argtypes = []
+        L.mkv_last_hip_error.restype = i
+        L.mkv_version.argtypes = []
+        L.mkv_version.restype = i
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != MKV_OK:
+        msg = lib().mkv_status_string(status).decode()
+        if status == MKV_ERR_HIP:
+            msg += f"; hip error {lib().mkv_last_hip_error()}"
+        raise MkvError(status, f"{what}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def group_bytes(bits: int, d: int) -> int:
+    return int(lib().mkv_group_bytes(bits, d))
+
+
+def pool_bytes(bits: int, B: int, Hkv: int, cap: int, d: int, C: int) -> int:
+    return int(lib().mkv_pool_bytes(bits, B, Hkv, cap, d, C))
+
+
+def workspace_bytes_route(B: int, T: int, D: int, I: int) -> int:
+    return int(lib().mkv_workspace_bytes(MKV_OP_ROUTE, B, T, D, I, 0, None))
+
+
+def workspace_bytes_attention(B: int, Hq: int, Hkv: int, d: int, C: int, caps: Sequence[int]) -> int:
+    arr = (ctypes.c_int * 3)(*caps)
+    return int(lib().mkv_workspace_bytes(MKV_OP_ATTENTION, B, Hq, Hkv, d, C, arr))
+
+
+class RouteTables:
+    """Device routing tables of B sequences with room for n_max chunks."""
+
+    def __init__(self, B: int, n_max: int, device="cuda"):
+        self.B, self.n_max = B, n_max
+        self.chunk_bits = torch.zeros((B, n_max), dtype=torch.uint8, device=device)
+        self.chunk_rank = torch.zeros((B, n_max), dtype=torch.int32, device=device)
+        self.perm = torch.zeros((B, n_max), dtype=torch.int32, device=device)
+        self.seg_count = torch.zeros((B, 3), dtype=torch.int32, device=device)
+
+    def c(self) -> MkvTables:
+        return MkvTables(self.chunk_bits.data_ptr(), self.chunk_rank.data_ptr(), self.perm.data_ptr(),
+                         self.seg_count.data_ptr(), self.n_max)
+
+
+class PackedCache:
+    """One layer's packed pools.  caps[k] = slots per (sequence, head) in the
+    FP16 / INT4 / INT2 pool.  seg_count is the routing tables' (shared by
+    every layer: routing sharing)."""
+
+    def __init__(self, B: int, Hkv: int, d: int, C: int, caps: Sequence[int],
+                 seg_count: torch.Tensor, device="cuda"):
+        self.B, self.Hkv, self.d, self.C = B, Hkv, d, C
+        self.caps = [int(c) for c in caps]
+        self.pools = []
+        for k, bits in enumerate(EXPERT_BITS):
+            nbytes = pool_bytes(bits, B, Hkv, self.caps[k], d, C)
+            self.pools.append(torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device))
+        self.seg_count = seg_count
+        self.overflow = torch.zeros(4, dtype=torch.int32, device=device)
+
+    def c(self) -> MkvCache:
+        cc = MkvCache()
+        cc.B, cc.Hkv, cc.d, cc.C = self.B, self.Hkv, self.d, self.C
+        for k in range(3):
+            cc.cap[k] = self.caps[k]
+            cc.pool[k] = self.pools[k].data_ptr()
+        cc.seg_count = self.seg_count.data_ptr()
+        cc.overflow = self.overflow.data_ptr()
+        return cc
+
+    def nbytes(self) -> int:
+        return sum(p.numel() for p in self.pools)
+
+
+def route_chunks(tables: RouteTables, C: int, *, x: torch.Tensor = None, w12: torch.Tensor = None,
+                 w3: torch.Tensor = None, b3: torch.Tensor = None, logits: torch.Tensor = None,
+                 logits_in: bool = False, freeze_first: bool = True, chunk_offset: int = 0,
+                 append: bool = False, token_expert: torch.Tensor = None,
+                 workspace: torch.Tensor = None, stream=None):
+    """mkv_route_chunks.  Router mode: x [B,T,D] bf16, w12 [2I,D] bf16, w3 [3,I]
+    f32, b3 [3] f32; logits (optional) receives [B,T,3].  Logits-in mode:
+    logits [B,T,3] f32 is the input."""
+    flags = (MKV_FREEZE_FIRST if freeze_first else 0) | (MKV_LOGITS_IN if logits_in else 0) \
+        | (MKV_APPEND if append else 0)
+    if logits_in:
+        B, T = logits.shape[0], logits.shape[1]
+        D = I = 0
+    else:
+        B, T, D = x.shape
+        I = w12.shape[0] // 2
+        if workspace is None:
+            workspace = torch.empty(workspace_bytes_route(B, T, D, I), dtype=torch.uint8, device=x.device)
+    tab = tables.c()
+    st = lib().mkv_route_chunks(_ptr(x), _ptr(w12), _ptr(w3), _ptr(b3), _ptr(logits), B, T, D, I, C, flags,
+                                _ptr(token_expert), ctypes.byref(tab), chunk_offset, _ptr(workspace),
+                                0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check(st, "mkv_route_chunks")
+
+
+def quantize_pack_kv(k: torch.Tensor, v: torch.Tensor, tables: RouteTables, cache: PackedCache,
+                     chunk_offset: int = 0, stream=None):
+    """mkv_quantize_pack_kv: k, v [B, Hkv, T, d] fp16 (T = new chunks * C)."""
+    T = k.shape[2]
+    tab = tables.c()
+    cc = cache.c()
+    st = lib().mkv_quantize_pack_kv(_ptr(k), _ptr(v), T, chunk_offset, ctypes.byref(tab),
+                                    ctypes.byref(cc), _stream(stream))
+    _check(st, "mkv_quantize_pack_kv")
+
+
+def mixed_kv_decode_attention(q: torch.Tensor, cache: PackedCache, out: torch.Tensor = None,
+                              tail_k: torch.Tensor = None, tail_v: torch.Tensor = None,
+                              workspace: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """mkv_mixed_kv_decode_attention: q [B, Hq, d] fp16 -> out [B, Hq, d] f32."""
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes_attention(B, Hq, cache.Hkv, d, cache.C, cache.caps),
+                                dtype=torch.uint8, device=q.device)
+    tail_len = 0 if tail_k is None else tail_k.shape[2]
+    cc = cache.c()
+    st = lib().mkv_mixed_kv_decode_attention(_ptr(q), Hq, ctypes.byref(cc), _ptr(tail_k), _ptr(tail_v),
+                                             tail_len, _ptr(out), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "mkv_mixed_kv_decode_attention")
+    return out

@@ -1,0 +1,247 @@
+/*
+ * mkv.h — C ABI of libmkv.so: chunk-adaptive mixed-precision KV cache on
+ * AMD MI355X (gfx950).
+ *
+ * The method (web sources, cited by page title and section):
+ *   - "MoQAE: Mixed-Precision Quantization for Long-Context LLM Inference via
+ *     Mixture of Quantization-Aware Experts" (Paper-Notes, ACL 2025):
+ *       "Overall framework": text is split into equal-length chunks; a router
+ *       scores every token against quantization "experts"; a vote inside each
+ *       chunk picks the chunk's bitwidth; the KV cache is quantized at that
+ *       bitwidth; attention then runs as usual.
+ *       "Key designs": experts are FP16, INT4, INT2; router MLP over a chunk's
+ *       hidden states; routing freezing (chunk 0 stays FP16); routing sharing
+ *       (one routing for every block).
+ *       "Related work" (KIVI): keys have outlier channels, so keys are
+ *       quantized per channel.
+ *   - Cocktail abstract (scholarfeed author page): chunks are reordered
+ *     before quantization so that chunks of one bitwidth are contiguous and
+ *     attention runs chunk by chunk without mixed-precision inefficiency.
+ *
+ * Three calls make the hot path:
+ *   mkv_route_chunks              router -> per-token expert -> chunk vote ->
+ *                                 freezing -> stable reorder tables
+ *   mkv_quantize_pack_kv          K/V of routed chunks -> packed segment pools
+ *   mkv_mixed_kv_decode_attention one query per sequence and query head over
+ *                                 the packed pools (+ optional fp16 tail)
+ *
+ * Conventions shared by every call
+ *   - Every pointer to tensor data is a DEVICE pointer; structs are passed by
+ *     HOST pointer and hold device pointers.  The caller allocates and owns
+ *     every buffer and keeps it alive until the stream work is done; the
+ *     library allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream) and the call returns without synchronising.
+ *   - Return value: MKV_OK (0) or a negative MKV_ERR_*.  Arguments are
+ *     checked before anything is launched, so an argument error leaves every
+ *     output untouched.  MKV_ERR_HIP means a HIP call failed; the HIP error
+ *     code of the last such failure on the calling thread is returned by
+ *     mkv_last_hip_error().
+ *   - Every device buffer must be 16-byte aligned.
+ *   - Bitwidths are 16 (FP16 expert, index 0), 4 (INT4, index 1) and
+ *     2 (INT2, index 2).  Expert index order is precision order.
+ */
+#ifndef MKV_H_
+#define MKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define MKV_OK               0
+#define MKV_ERR_ARG         -1  /* null pointer, bad size, misalignment     */
+#define MKV_ERR_UNSUPPORTED -2  /* shape outside what the kernels handle    */
+#define MKV_ERR_WORKSPACE   -3  /* workspace missing or too small           */
+#define MKV_ERR_HIP         -4  /* a HIP runtime call failed                */
+
+/* ---- flags for mkv_route_chunks ---------------------------------------- */
+#define MKV_FREEZE_FIRST 0x1u /* routing freezing: chunk 0 of each sequence
+                                 becomes FP16 (MoQAE, "Key designs")       */
+#define MKV_LOGITS_IN    0x2u /* skip the router: `logits` holds the final
+                                 per-token expert scores to vote on        */
+#define MKV_APPEND       0x4u /* the routed chunks start at chunk_offset;
+                                 tables for chunks [0, chunk_offset) are
+                                 kept and the reorder covers them too      */
+
+/* ---- workspace query ops ------------------------------------------------ */
+#define MKV_OP_ROUTE     1
+#define MKV_OP_ATTENTION 2
+
+/* Routing tables of a batch of sequences (routing sharing: one table serves
+ * every layer and head).  All arrays are device memory, row stride n_max:
+ *   chunk_bits [B][n_max] u8   16 / 4 / 2 for each chunk (in chunk order)
+ *   chunk_rank [B][n_max] i32  slot of the chunk inside its bitwidth segment
+ *   perm       [B][n_max] i32  segment-order position -> chunk index
+ *                              (FP16 segment, then INT4, then INT2; chunk
+ *                              order kept inside a segment)
+ *   seg_count  [B][3]     i32  chunks in the FP16, INT4 and INT2 segments   */
+typedef struct mkv_tables {
+    uint8_t* chunk_bits;
+    int32_t* chunk_rank;
+    int32_t* perm;
+    int32_t* seg_count;
+    int n_max;
+} mkv_tables;
+
+/* One layer's packed cache.  pool[k] (k = 0 FP16, 1 INT4, 2 INT2) is device
+ * memory of mkv_pool_bytes(k-th bitwidth, B, Hkv, cap[k], d, C) bytes, laid
+ * out [B][Hkv][cap[k] slots][C/32 groups][group block].  The chunk of
+ * sequence b with bitwidth index k and rank r lives at slot r of every head
+ * (b, h).  The segment of (b, h, k) is therefore one contiguous run of
+ * seg_count[b][k]*C/32 group blocks.
+ *
+ * A group block holds 32 consecutive tokens of one (sequence, KV head).
+ * Let S = d/8 ("lane slots"), NG = d/32 (value groups per token) and let
+ * a "row" of a section be S 16-byte cells, cell L belonging to lane slot L.
+ * A group block is four sections in this order, each section being a run of
+ * rows (row index = "load index"):
+ *
+ *   INT-b (b = 4 or 2), F = 32/b codes per 32-bit word, LSB first:
+ *     K codes   rows 0 .. b*2-1: lane slot L owns channels 8L..8L+7; for
+ *               channel j = 8L + 4*(row & 1) + e (e = dword in the cell) the
+ *               cell holds word w = row >> 1 of that channel.  Field i of word
+ *               w of channel j (lane slot L) is the key code of token
+ *               ((F*w + i) XOR f_S(L)) of the group, where
+ *                 f_16(L) = 24*L3 ^ 14*L2 ^ 4*L1 ^ 2*L0  (d = 128)
+ *                 f_8(L)  = 28*L2 ^ 8*L1 ^ 4*L0           (d = 64)
+ *               and Lk is bit k of L.  Key quantization groups run along
+ *               tokens: one (scale, min) per channel for the 32 tokens.
+ *     K meta    4 rows: row 0 / 1 = scale of channels 8L+0..3 / 8L+4..7,
+ *               row 2 / 3 = min of the same channels (float32).
+ *     V codes   b*2 rows: lane slot L has value group G = L % NG and token
+ *               quarter tq = L / NG and covers tokens t_m = tq + 4m,
+ *               m = 0..7, channels 32G..32G+31.  INT4: row m holds words
+ *               u = 0..3 of token t_m, word u = channels 32G+8u .. +7.
+ *               INT2: row m holds words of tokens t_{2m}, t_{2m+1} (two each,
+ *               word u = channels 32G+16u .. +15).  Value groups run along
+ *               channels: one (scale, min) per (token, 32 channels).
+ *     V meta    4 rows: row m holds (scale, min) of token t_{2m} then
+ *               (scale, min) of token t_{2m+1}, for group G (float32).
+ *   FP16 (bit-for-bit copies):
+ *     K         32 rows: row r holds channels 8L..8L+7 of token r XOR f_S(L).
+ *     V         32 rows: row r holds channels 32G + 8*(r & 3) .. +7 of token
+ *               t_{r >> 2} (G, t_m as for INT-b values).
+ *   Group block bytes: FP16 64*S*16, INT4 24*S*16, INT2 16*S*16.
+ * The layout lets each lane of a 64-wide wavefront issue whole-row 16-byte
+ * loads that are contiguous across the lane slots of a row.  Quantization
+ * itself (which values share a scale) does not depend on the layout.     */
+typedef struct mkv_cache {
+    int B, Hkv, d, C;
+    int cap[3];                 /* slots per (sequence, head) in each pool  */
+    void* pool[3];              /* device; pool[k] may be NULL if cap[k]==0 */
+    const int32_t* seg_count;   /* device [B][3] (usually tables.seg_count) */
+    int32_t* overflow;          /* device i32 or NULL: set to 1 by
+                                   mkv_quantize_pack_kv when a chunk's rank
+                                   does not fit cap[k] (that chunk is then
+                                   not written)                             */
+} mkv_cache;
+
+/* ------------------------------------------------------------------------
+ * 1. mkv_route_chunks — router, chunk vote, routing freezing, reorder.
+ *    MoQAE "Key designs" (Quantization-Aware Experts; routing freezing;
+ *    routing sharing) and Cocktail abstract (reorder before quantization).
+ *
+ * Routes T tokens (= T/C new chunks) of each of B sequences.  Per token:
+ *   z = SiLU((x W1^T) .* (x W2^T)) W3^T + b3        (3 logits, fp32)
+ * with bf16 inputs and fp32 accumulation (MFMA); the expert is the argmax
+ * (ties to the lower index).  Per chunk: plurality vote over its C tokens
+ * (ties to the lower index); with MKV_FREEZE_FIRST chunk 0 becomes FP16.
+ * The chunk bitwidths land in tab->chunk_bits[b][chunk_offset + c]; then
+ * chunk_rank, perm and seg_count are recomputed over chunks
+ * [0, chunk_offset + T/C) of each sequence (stable partition FP16, INT4, INT2).
+ *
+ *   x_bf16     [B][T][D] bf16 hidden states (ignored with MKV_LOGITS_IN)
+ *   w12_bf16   [2I][D] bf16, rows 0..I-1 = W1, rows I..2I-1 = W2
+ *   w3         [3][I] fp32;   b3 [3] fp32
+ *   logits     [B][T][3] fp32: output if non-NULL; with MKV_LOGITS_IN it is
+ *              the input (final scores, b3 not added) and must be non-NULL
+ *   token_expert [B][T] u8 output (expert index per token) or NULL
+ *   chunk_offset must be 0 unless MKV_APPEND is set; chunk_offset + T/C
+ *              must not exceed tab->n_max.
+ *   workspace  device scratch of at least
+ *              mkv_workspace_bytes(MKV_OP_ROUTE, B, T, D, I, ...) bytes.
+ * Limits: T % C == 0, C % 32 == 0, 32 <= C <= 1024; D % 64 == 0;
+ *         I % 64 == 0 (router mode).
+ * ---------------------------------------------------------------------- */
+int mkv_route_chunks(const void* x_bf16, const void* w12_bf16,
+                     const float* w3, const float* b3, float* logits,
+                     int B, int T, int D, int I, int C, unsigned flags,
+                     uint8_t* token_expert, const mkv_tables* tab,
+                     int chunk_offset, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * 2. mkv_quantize_pack_kv — quantize and pack the K/V of routed chunks.
+ *    MoQAE "Overall framework" (cache quantized at the voted bitwidth) and
+ *    "Related work" (keys per channel); Cocktail abstract (chunks written to
+ *    their bitwidth's contiguous segment).
+ *
+ *   k_fp16, v_fp16  [B][Hkv][T][d] fp16, the T = n_new*C tokens of chunks
+ *                   chunk_offset .. chunk_offset+n_new-1 of each sequence
+ *   tab             tables from mkv_route_chunks (chunk_bits, chunk_rank)
+ *   cache           destination; B, Hkv, d, C are taken from it
+ * FP16 chunks are copied bit for bit.  INT-b chunks (b = 4, 2, L = 2^b-1)
+ * use asymmetric min-max codes on groups of 32 values (keys: 32 tokens of
+ * one channel; values: 32 channels of one token), in float32 with one
+ * rounding per operation:
+ *   mn = min, mx = max (a -0 extreme becomes +0), s = (mx - mn) / L, r = 1 / s,
+ *   code = clamp(round_half_even((x - mn) * r), 0, L); s == 0 -> codes 0.
+ * Dequantization is x = code * s + mn.
+ * Limits: as for the cache; T % C == 0.
+ * ---------------------------------------------------------------------- */
+int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T,
+                         int chunk_offset, const mkv_tables* tab,
+                         const mkv_cache* cache, void* stream);
+
+/* ------------------------------------------------------------------------
+ * 3. mkv_mixed_kv_decode_attention — one decode step over the mixed cache.
+ *    MoQAE "Overall framework" (ordinary attention after quantization) and
+ *    Cocktail abstract (chunk-level computation over reordered segments).
+ *
+ * For each sequence b and query head hq (KV head h = hq / (Hq/Hkv)):
+ *   out[b][hq] = softmax(q k^T / sqrt(d)) v
+ * over every cached token of (b, h) (all segments, in any order: attention
+ * does not depend on key order) plus the tail_len fp16 tokens of the tail.
+ * Cached values are dequantized in registers; accumulation is fp32.  Work
+ * is split over (sequence, KV head, single-bitwidth tile of groups) and the
+ * tile partials are merged with a log-sum-exp combine.
+ *
+ *   q_fp16      [B][Hq][d] fp16
+ *   tail_k/v    [B][Hkv][tail_len][d] fp16, or NULL when tail_len == 0
+ *   out         [B][Hq][d] fp32
+ *   workspace   at least mkv_workspace_bytes(MKV_OP_ATTENTION, ...) bytes
+ * Limits: d in {64, 128}; Hq/Hkv in {1, 2, 4, 8}; 0 <= tail_len < 4096.
+ * A (b, h) with no cached token and tail_len == 0 yields zeros.
+ * ---------------------------------------------------------------------- */
+int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq,
+                                  const mkv_cache* cache,
+                                  const void* tail_k_fp16,
+                                  const void* tail_v_fp16, int tail_len,
+                                  float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* ---- helpers -------------------------------------------------------------
+ * mkv_workspace_bytes: scratch needed by an op.
+ *   MKV_OP_ROUTE:     a = B, b = T, c = D, e = I (f, g unused)
+ *   MKV_OP_ATTENTION: a = B, b = Hq, c = Hkv, e = d, f = C, and `cache_caps`
+ *                     points to the cache's cap[3] (host memory)
+ * Returns 0 for an unknown op or invalid sizes.                          */
+size_t mkv_workspace_bytes(int op, int a, int b, int c, int e, int f,
+                           const int* cache_caps);
+
+/* Bytes of one group block (32 tokens of one head) and of one pool. */
+size_t mkv_group_bytes(int bits, int d);
+size_t mkv_pool_bytes(int bits, int B, int Hkv, int cap, int d, int C);
+
+const char* mkv_status_string(int status);
+int mkv_last_hip_error(void);
+int mkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MKV_H_ */

@@ -40,7 +40,8 @@ the design notes):
       each tensor's quantization axis (keys: 32 tokens of one channel,
       values: 32 channels of one token, following the KIVI note).
       s = fl((mx - mn) / L), r = fl(1 / s), code = clamp(rne(fl(fl(x - mn) * r)), 0, L),
-      mn canonicalised to +0; s == 0 gives all-zero codes.
+      a -0 extreme (mn or mx) is canonicalised to +0, so s and mn never carry
+      a sign that depends on reduction order; s == 0 gives all-zero codes.
   R8  Attention is ordinary softmax attention over the dequantized cache
       (x_hat = code * s + mn), no mask, keys already position-encoded.
 """
@@ -175,6 +176,7 @@ def quantize_groups(g: np.ndarray, bits: int):
     mn = x.min(axis=-1)
     mx = x.max(axis=-1)
     mn = (mn + np.float32(0.0)).astype(np.float32)      # -0 -> +0
+    mx = (mx + np.float32(0.0)).astype(np.float32)      # -0 -> +0
     s = ((mx - mn).astype(np.float32) / L).astype(np.float32)
     zero = s == np.float32(0.0)
     safe = np.where(zero, np.float32(1.0), s).astype(np.float32)

@@ -1,0 +1,165 @@
+"""Test-side reader of the packed-cache layout documented in include/mkv.h,
+written from that documentation in numpy.  It shares no code with the HIP
+library: it turns pool bytes back into logical codes, scales and minima so
+that tests can compare them with the oracle.
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+GROUP = 32
+
+
+def tok_xor(S: int, L: int) -> int:
+    b = [(L >> i) & 1 for i in range(4)]
+    if S == 16:
+        return (24 * b[3]) ^ (14 * b[2]) ^ (4 * b[1]) ^ (2 * b[0])
+    if S == 8:
+        return (28 * b[2]) ^ (8 * b[1]) ^ (4 * b[0])
+    raise ValueError(S)
+
+
+def section_rows(bits: int):
+    if bits == 16:
+        return 32, 0, 32, 0
+    return 2 * bits, 4, 2 * bits, 4
+
+
+def group_bytes(bits: int, d: int) -> int:
+    return sum(section_rows(bits)) * (d // 8) * 16
+
+
+def chunk_bytes(bits: int, d: int, C: int) -> int:
+    return group_bytes(bits, d) * (C // GROUP)
+
+
+@functools.lru_cache(maxsize=None)
+def _maps(bits: int, d: int):
+    """Index maps from (row, lane slot, dword, field) to (token, channel)."""
+    S, NG = d // 8, d // 32
+    KC, KM, VC, VM = section_rows(bits)
+    m = {}
+    if bits == 16:
+        # K: row r, slot L, half-word e8 (0..7) -> token r^f(L), channel 8L+e8
+        kt = np.zeros((32, S, 8), np.int64)
+        kc = np.zeros((32, S, 8), np.int64)
+        vt = np.zeros((32, S, 8), np.int64)
+        vc = np.zeros((32, S, 8), np.int64)
+        for r in range(32):
+            for L in range(S):
+                G, tq = L % NG, L // NG
+                for e in range(8):
+                    kt[r, L, e] = r ^ tok_xor(S, L)
+                    kc[r, L, e] = 8 * L + e
+                    vt[r, L, e] = tq + 4 * (r >> 2)
+                    vc[r, L, e] = 32 * G + 8 * (r & 3) + e
+        m.update(kt=kt, kc=kc, vt=vt, vc=vc)
+        return m
+    F = 32 // bits
+    kt = np.zeros((KC, S, 4, F), np.int64)
+    kc = np.zeros((KC, S, 4, F), np.int64)
+    for row in range(KC):
+        for L in range(S):
+            for e in range(4):
+                for i in range(F):
+                    kt[row, L, e, i] = (F * (row >> 1) + i) ^ tok_xor(S, L)
+                    kc[row, L, e, i] = 8 * L + 4 * (row & 1) + e
+    vt = np.zeros((VC, S, 4, F), np.int64)
+    vc = np.zeros((VC, S, 4, F), np.int64)
+    for row in range(VC):
+        for L in range(S):
+            G, tq = L % NG, L // NG
+            for dw in range(4):
+                for i in range(F):
+                    if bits == 4:
+                        mm, u = row, dw
+                        vt[row, L, dw, i] = tq + 4 * mm
+                        vc[row, L, dw, i] = 32 * G + 8 * u + i
+                    else:
+                        mm, u = 2 * row + (dw >> 1), dw & 1
+                        vt[row, L, dw, i] = tq + 4 * mm
+                        vc[row, L, dw, i] = 32 * G + 16 * u + i
+    # meta: row mr, slot L, float f4 (0..3) -> token, group, is_min
+    mt = np.zeros((4, S, 4), np.int64)
+    mg = np.zeros((4, S, 4), np.int64)
+    for mr in range(4):
+        for L in range(S):
+            G, tq = L % NG, L // NG
+            for f4 in range(4):
+                mt[mr, L, f4] = tq + 4 * (2 * mr + (f4 >> 1))
+                mg[mr, L, f4] = G
+    m.update(kt=kt, kc=kc, vt=vt, vc=vc, mt=mt, mg=mg)
+    return m
+
+
+def decode_blocks(blocks: np.ndarray, bits: int, d: int) -> dict:
+    """Group blocks uint8 [N, group_bytes] -> logical contents with a leading N.
+    INT-b: kq [N,32,d], ks [N,d], km [N,d], vq [N,32,d], vs [N,32,d/32], vm.
+    FP16:  k [N,32,d], v [N,32,d] float16."""
+    S, NG = d // 8, d // 32
+    KC, KM, VC, VM = section_rows(bits)
+    N = blocks.shape[0]
+    cells = np.ascontiguousarray(blocks).reshape(N, KC + KM + VC + VM, S, 16)
+    m = _maps(bits, d)
+    if bits == 16:
+        kh = cells[:, :KC].copy().view(np.float16).reshape(N, KC, S, 8)
+        vh = cells[:, KC:].copy().view(np.float16).reshape(N, VC, S, 8)
+        k = np.zeros((N, 32, d), np.float16)
+        v = np.zeros((N, 32, d), np.float16)
+        k[:, m["kt"], m["kc"]] = kh
+        v[:, m["vt"], m["vc"]] = vh
+        return {"bits": 16, "k": k, "v": v}
+    F = 32 // bits
+    mask = np.uint32((1 << bits) - 1)
+    shifts = (np.arange(F, dtype=np.uint32) * np.uint32(bits))
+    kw = cells[:, :KC].copy().view(np.uint32).reshape(N, KC, S, 4)
+    kfield = (kw[..., None] >> shifts) & mask
+    kq = np.zeros((N, 32, d), np.uint8)
+    kq[:, m["kt"], m["kc"]] = kfield.astype(np.uint8)
+    kmeta = cells[:, KC:KC + 4].copy().view(np.float32).reshape(N, 4, S, 4)
+    ks = np.concatenate([kmeta[:, 0], kmeta[:, 1]], axis=-1)          # [N, S, 8]
+    km = np.concatenate([kmeta[:, 2], kmeta[:, 3]], axis=-1)
+    ks = ks.reshape(N, d)
+    km = km.reshape(N, d)
+    vw = cells[:, KC + KM:KC + KM + VC].copy().view(np.uint32).reshape(N, VC, S, 4)
+    vfield = (vw[..., None] >> shifts) & mask
+    vq = np.zeros((N, 32, d), np.uint8)
+    vq[:, m["vt"], m["vc"]] = vfield.astype(np.uint8)
+    vmeta = cells[:, KC + KM + VC:].copy().view(np.float32).reshape(N, 4, S, 4)
+    vs = np.zeros((N, 32, NG), np.float32)
+    vm = np.zeros((N, 32, NG), np.float32)
+    is_scale = (np.arange(4) % 2 == 0)
+    mt, mg = m["mt"], m["mg"]
+    vs[:, mt[..., is_scale], mg[..., is_scale]] = vmeta[..., is_scale]
+    vm[:, mt[..., ~is_scale], mg[..., ~is_scale]] = vmeta[..., ~is_scale]
+    return {"bits": bits, "kq": kq, "ks": ks, "km": km, "vq": vq, "vs": vs, "vm": vm}
+
+
+def decode_chunks(pool: np.ndarray, bits: int, Hkv: int, cap: int, d: int, C: int,
+                  bh_slots) -> list:
+    """Decode the chunks at (b, h, slot) triples; returns dicts shaped like the
+    oracle's quantize_chunk output: kq [C,d], ks [C/32,d], km, vq [C,d],
+    vs [C,d/32], vm  (FP16: k, v [C,d])."""
+    gb = group_bytes(bits, d)
+    gpc = C // GROUP
+    idx = []
+    for (b, h, slot) in bh_slots:
+        base = ((b * Hkv + h) * cap + slot) * gpc
+        idx.extend(range(base, base + gpc))
+    if not idx:
+        return []
+    blocks = pool.reshape(-1, gb)[np.asarray(idx)]
+    dec = decode_blocks(blocks, bits, d)
+    out = []
+    for n in range(len(bh_slots)):
+        sl = slice(n * gpc, (n + 1) * gpc)
+        if bits == 16:
+            out.append({"bits": 16, "k": dec["k"][sl].reshape(C, d), "v": dec["v"][sl].reshape(C, d)})
+        else:
+            out.append({"bits": bits,
+                        "kq": dec["kq"][sl].reshape(C, d), "ks": dec["ks"][sl], "km": dec["km"][sl],
+                        "vq": dec["vq"][sl].reshape(C, d),
+                        "vs": dec["vs"][sl].reshape(C, d // 32), "vm": dec["vm"][sl].reshape(C, d // 32)})
+    return out

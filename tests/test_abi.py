@@ -1,0 +1,145 @@
+"""CPU checks of the C ABI: the library loads, exports every call the header
+declares, sizes its buffers as documented and rejects bad arguments before
+launching anything (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunk_mixed_precision_amd import mkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mkv.LIB_PATH), reason="libmkv.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("mkv_route_chunks", "mkv_quantize_pack_kv", "mkv_mixed_kv_decode_attention"):
+        assert n in names
+
+
+def test_every_declared_function_is_exported():
+    L = mkv.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(mkv.EXPORTED) <= set(declared_functions())
+
+
+def test_status_strings_and_version():
+    L = mkv.lib()
+    assert L.mkv_version() >= 1
+    for s in (0, -1, -2, -3, -4):
+        assert len(L.mkv_status_string(s)) > 0
+    assert L.mkv_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("bits,d,expect", [(16, 128, 16384), (4, 128, 6144), (2, 128, 4096),
+                                           (16, 64, 8192), (4, 64, 3072), (2, 64, 2048),
+                                           (8, 128, 0), (4, 96, 0)])
+def test_group_bytes(bits, d, expect):
+    # 32 tokens x per-token bytes: FP16 4d; INT-b 2*(d*b/8 + d/32*8)
+    assert mkv.group_bytes(bits, d) == expect
+
+
+def test_pool_and_workspace_bytes():
+    assert mkv.pool_bytes(4, 2, 3, 5, 128, 256) == 2 * 3 * 5 * 8 * 6144
+    assert mkv.workspace_bytes_route(2, 1024, 256, 128) == (128 // 64) * 2 * 1024 * 3 * 4
+    w = mkv.workspace_bytes_attention(1, 32, 32, 128, 256, [4, 115, 9])
+    assert w > 0
+    assert mkv.workspace_bytes_attention(1, 3, 2, 128, 256, [1, 1, 1]) == 0
+
+
+def _tables(n_max=8):
+    return mkv.MkvTables(0x1000, 0x2000, 0x3000, 0x4000, n_max)
+
+
+def _cache(d=128, C=128, caps=(1, 1, 1)):
+    c = mkv.MkvCache()
+    c.B, c.Hkv, c.d, c.C = 1, 2, d, C
+    for k in range(3):
+        c.cap[k] = caps[k]
+        c.pool[k] = 0x10000 * (k + 1)
+    c.seg_count = 0x5000
+    c.overflow = None
+    return c
+
+
+def route(**kw):
+    a = dict(x=0x100, w12=0x200, w3=0x300, b3=0x400, logits=None, B=1, T=256, D=256, I=128, C=128,
+             flags=mkv.MKV_FREEZE_FIRST, te=None, tab=_tables(), off=0, ws=None, wsb=0)
+    a.update(kw)
+    tab = a["tab"]
+    return mkv.lib().mkv_route_chunks(a["x"], a["w12"], a["w3"], a["b3"], a["logits"], a["B"], a["T"], a["D"],
+                                      a["I"], a["C"], a["flags"], a["te"],
+                                      None if tab is None else ctypes.byref(tab), a["off"], a["ws"], a["wsb"], None)
+
+
+def test_route_argument_errors():
+    E = mkv
+    assert route(tab=None) == E.MKV_ERR_ARG
+    assert route(x=None) == E.MKV_ERR_ARG
+    assert route(C=48) == E.MKV_ERR_UNSUPPORTED
+    assert route(T=200) == E.MKV_ERR_UNSUPPORTED
+    assert route(D=100) == E.MKV_ERR_UNSUPPORTED
+    assert route(I=100) == E.MKV_ERR_UNSUPPORTED
+    assert route(x=0x101) == E.MKV_ERR_ARG                       # misaligned
+    assert route(off=1) == E.MKV_ERR_ARG                         # offset without MKV_APPEND
+    assert route(tab=_tables(n_max=1)) == E.MKV_ERR_ARG          # 2 chunks > n_max
+    assert route(flags=0x80) == E.MKV_ERR_ARG
+    assert route() == E.MKV_ERR_WORKSPACE                        # no workspace
+    assert route(ws=0x9000, wsb=16) == E.MKV_ERR_WORKSPACE       # too small
+    assert route(flags=mkv.MKV_LOGITS_IN, logits=None) == E.MKV_ERR_ARG
+    assert route(flags=mkv.MKV_APPEND, off=8) == E.MKV_ERR_ARG   # 8 + 2 > n_max
+
+
+def quant(cache=None, tab=None, T=256, off=0, k=0x100, v=0x200):
+    cache = cache or _cache()
+    tab = tab or _tables()
+    return mkv.lib().mkv_quantize_pack_kv(k, v, T, off, ctypes.byref(tab), ctypes.byref(cache), None)
+
+
+def test_quantize_argument_errors():
+    E = mkv
+    assert quant(k=None) == E.MKV_ERR_ARG
+    assert quant(v=0x208) == E.MKV_ERR_ARG
+    assert quant(cache=_cache(d=96)) == E.MKV_ERR_UNSUPPORTED
+    assert quant(cache=_cache(C=48)) == E.MKV_ERR_UNSUPPORTED
+    assert quant(T=200) == E.MKV_ERR_ARG
+    assert quant(off=7) == E.MKV_ERR_ARG                        # 7 + 2 > n_max
+    c = _cache()
+    c.pool[1] = 0x10008                                          # misaligned pool
+    assert quant(cache=c) == E.MKV_ERR_ARG
+    c = _cache()
+    c.cap[2] = -1
+    assert quant(cache=c) == E.MKV_ERR_ARG
+    c = _cache()
+    c.seg_count = None
+    assert quant(cache=c) == E.MKV_ERR_ARG
+
+
+def attn(Hq=2, cache=None, tail_len=0, tk=None, tv=None, out=0x700, ws=None, wsb=0, q=0x600):
+    cache = cache or _cache()
+    return mkv.lib().mkv_mixed_kv_decode_attention(q, Hq, ctypes.byref(cache), tk, tv, tail_len, out, ws, wsb,
+                                                   None)
+
+
+def test_attention_argument_errors():
+    E = mkv
+    assert attn(q=None) == E.MKV_ERR_ARG
+    assert attn(out=0x704) == E.MKV_ERR_ARG
+    assert attn(Hq=3) == E.MKV_ERR_ARG                          # not a multiple of Hkv
+    assert attn(Hq=16) == E.MKV_ERR_UNSUPPORTED                 # 8 query heads per KV head
+    assert attn(cache=_cache(d=256)) == E.MKV_ERR_UNSUPPORTED
+    assert attn(tail_len=5) == E.MKV_ERR_ARG                    # tail pointers missing
+    assert attn(tail_len=4096, tk=0x800, tv=0x900) == E.MKV_ERR_ARG
+    assert attn() == E.MKV_ERR_WORKSPACE
+    assert attn(ws=0x9000, wsb=64) == E.MKV_ERR_WORKSPACE

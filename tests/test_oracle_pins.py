@@ -378,6 +378,7 @@ def _quant_variant(mistake):
         mx = x.max(axis=-1)
         if mistake != "no_zero_canon":
             mn = (mn + np.float32(0.0)).astype(np.float32)
+            mx = (mx + np.float32(0.0)).astype(np.float32)
         s = ((mx - mn).astype(np.float32) / L).astype(np.float32)
         zero = s == 0
         safe = np.where(zero, np.float32(1.0), s).astype(np.float32)
@@ -400,6 +401,10 @@ def _quant_variant(mistake):
         qv[zero] = 0
         return qv.astype(np.uint8), s, mn
     return q
+
+
+def test_unmutated_variant_passes_the_pins():
+    check_quantizer_on_cases(_quant_variant(None))
 
 
 @pytest.mark.parametrize("mistake", ["divide", "half_away", "truncate", "no_zero_canon", "bad_levels"])
