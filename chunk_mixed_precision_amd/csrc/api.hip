@@ -20,18 +20,23 @@ inline int hip_status(hipError_t e) {
     return MKV_ERR_HIP;
 }
 
-// Groups per attention tile in each pool (FP16, INT4, INT2).  Tiles of one
-// bitwidth carry a similar number of bytes: 64 KB (FP16), 48 KB (INT4) and
-// 64 KB (INT2) at d = 128.
-inline void attn_tiles(int d, const int* cap, int C, int tg[3], int nt[3], int& nt_total) {
-    const int base[3] = {4, 8, 16};
-    nt_total = 0;
-    for (int k = 0; k < 3; ++k) {
-        tg[k] = d == 64 ? 2 * base[k] : base[k];
-        const long groups = (long)cap[k] * (C / mkv::kGroup);
-        nt[k] = (int)((groups + tg[k] - 1) / tg[k]);
-        nt_total += nt[k];
-    }
+// Attention work split.  The bytes of each (sequence, KV head) are cut into
+// parts of about per_wave bytes, one 64-lane wavefront per part; per_wave is
+// chosen so that the whole cache (at capacity) needs about kAttnWaves
+// wavefronts, i.e. one resident round on 256 CUs (8 per CU at the kernel's
+// register use), with a floor that keeps every wavefront busy for a while.
+constexpr long long kAttnWaves = 2048;
+constexpr long long kMinWaveBytes = 16384;
+
+inline void attn_split(int B, int Hkv, int d, const int* cap, int C, long long& per_wave, int& nt_total) {
+    const int bits[3] = {16, 4, 2};
+    long long bh_bytes = 0;
+    for (int k = 0; k < 3; ++k) bh_bytes += (long long)cap[k] * (C / mkv::kGroup) * (long long)mkv::group_bytes(bits[k], d);
+    const long long total = bh_bytes * B * Hkv;
+    per_wave = (total + kAttnWaves - 1) / kAttnWaves;
+    if (per_wave < kMinWaveBytes) per_wave = kMinWaveBytes;
+    const long long nw_max = (bh_bytes + per_wave - 1) / per_wave;
+    nt_total = (int)(3 * (nw_max > 0 ? nw_max : 1));
 }
 
 inline bool valid_cache(const mkv_cache* c) {
@@ -91,8 +96,9 @@ size_t mkv_workspace_bytes(int op, int a, int b, int c, int e, int f, const int*
     if (op == MKV_OP_ATTENTION) {
         const int B = a, Hq = b, Hkv = c, d = e, C = f;
         if (!caps || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (d != 64 && d != 128) || C <= 0 || C % 32) return 0;
-        int tg[3], nt[3], ntt;
-        attn_tiles(d, caps, C, tg, nt, ntt);
+        long long pw;
+        int ntt;
+        attn_split(B, Hkv, d, caps, C, pw, ntt);
         return (size_t)B * Hkv * ntt * (Hq / Hkv) * (d + 4) * sizeof(float) + 16;
     }
     return 0;
@@ -197,23 +203,14 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq, const mkv_cache* c
     }
     ap.seg_count = cache->seg_count;
     ap.B = cache->B; ap.Hkv = cache->Hkv; ap.Hq = Hq; ap.C = cache->C;
-    attn_tiles(cache->d, cache->cap, cache->C, ap.tg, ap.nt, ap.nt_total);
+    attn_split(cache->B, cache->Hkv, cache->d, cache->cap, cache->C, ap.per_wave, ap.nt_total);
     ap.part = static_cast<float*>(workspace);
+    ap.tail_k = static_cast<const uint16_t*>(tail_k_fp16);
+    ap.tail_v = static_cast<const uint16_t*>(tail_v_fp16);
+    ap.tail_len = tail_len;
+    ap.out = out;
     ap.qscale = (float)(1.4426950408889634 / sqrt((double)cache->d));
-
-    mkv::CombineParams cp{};
-    cp.part = ap.part;
-    cp.seg_count = cache->seg_count;
-    cp.q = ap.q;
-    cp.tail_k = static_cast<const uint16_t*>(tail_k_fp16);
-    cp.tail_v = static_cast<const uint16_t*>(tail_v_fp16);
-    cp.tail_len = tail_len;
-    cp.out = out;
-    cp.B = cache->B; cp.Hkv = cache->Hkv; cp.Hq = Hq; cp.C = cache->C;
-    for (int k = 0; k < 3; ++k) { cp.cap[k] = ap.cap[k]; cp.tg[k] = ap.tg[k]; cp.nt[k] = ap.nt[k]; }
-    cp.nt_total = ap.nt_total;
-    cp.qscale = ap.qscale;
-    return hip_status(mkv::launch_attention(ap, cp, cache->d, g, (hipStream_t)stream));
+    return hip_status(mkv::launch_attention(ap, cache->d, g, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -90,6 +90,35 @@ __device__ __forceinline__ void row_reduce_scatter(float* acc) {
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ float4 ldf4(const uint8_t* p) { return *reinterpret_cast<const float4*>(p); }
 
+__device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_cast(float4, u); }
+
+// Rows of one load phase.  INT-b: phase 0 = key codes + key meta, phase 1 =
+// value codes + value meta.  FP16: eight phases of 8 rows (key rows 0-7,
+// 8-15, 16-23, 24-31, then the value rows likewise).
+template <int BITS> __host__ __device__ constexpr int ph_rows() { return BITS == 16 ? 8 : 2 * BITS + 4; }
+template <int BITS> __host__ __device__ constexpr int n_phases() { return BITS == 16 ? 8 : 2; }
+
+template <int BITS, int D>
+__device__ __forceinline__ void load_phase(uint4* buf, const uint8_t* gp, int phase, int L) {
+    constexpr int NR = ph_rows<BITS>();
+    constexpr size_t ROWB = (size_t)(D / 8) * 16;
+    const uint8_t* src = gp + (size_t)phase * NR * ROWB + L * 16;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) buf[i] = ld16(src + i * ROWB);
+}
+
+// Combine the partials of two softmax runs: (m, l, o) <- (m, l, o) + (m2, l2, o2).
+template <int N>
+__device__ __forceinline__ void merge_run(float& m, float& l, float* o, float m2, float l2, const float* o2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    const float a = fast_exp2(m - mn), b = fast_exp2(m2 - mn);
+    l = l * a + l2 * b;
+#pragma unroll
+    for (int c = 0; c < N; ++c) o[c] = o[c] * a + o2[c] * b;
+    m = mn;
+}
+
 template <int BITS, int D, int HB>
 __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, int x, int g0, int g1) {
     constexpr int S = D / 8;
@@ -99,8 +128,8 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
     constexpr int NT = 32 / S;         // tokens per lane after the reduce-scatter
     constexpr int KCR = kc_rows(BITS);
     constexpr int VCR = vc_rows(BITS);
+    constexpr int NR = ph_rows<BITS>();
     constexpr size_t GB = group_bytes(BITS, D);
-    constexpr size_t ROWB = (size_t)S * 16;
 
     __shared__ float plds[R][32];
 
@@ -132,82 +161,14 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
 #pragma unroll
     for (int c = 0; c < 32; ++c) o[c] = 0.f;
 
-    for (int gbase = g0; gbase < g1; gbase += GPI) {
+    auto group_ptr = [&](int gbase) {
         const int gi = gbase + gslot;
-        const bool valid = gi < g1;
-        const uint8_t* gp = seg + (size_t)(valid ? gi : g1 - 1) * GB;
+        return seg + (size_t)(gi < g1 ? gi : g1 - 1) * GB;
+    };
 
-        // ---------------- scores
-        float acc[32];
-        if constexpr (BITS == 16) {
-            const half2_t q0 = as_h2(qw[0]), q1 = as_h2(qw[1]), q2 = as_h2(qw[2]), q3 = as_h2(qw[3]);
-#pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                const uint4 c = ld16(gp + r * ROWB + L * 16);
-                float a = __builtin_amdgcn_fdot2(as_h2(c.x), q0, 0.f, false);
-                a = __builtin_amdgcn_fdot2(as_h2(c.y), q1, a, false);
-                a = __builtin_amdgcn_fdot2(as_h2(c.z), q2, a, false);
-                a = __builtin_amdgcn_fdot2(as_h2(c.w), q3, a, false);
-                acc[r] = a;
-            }
-        } else {
-            uint4 kc[KCR];
-#pragma unroll
-            for (int i = 0; i < KCR; ++i) kc[i] = ld16(gp + i * ROWB + L * 16);
-            const uint8_t* kmp = gp + (size_t)km_row0(BITS) * ROWB + L * 16;
-            const float4 s0 = ldf4(kmp), s1 = ldf4(kmp + ROWB), m0 = ldf4(kmp + 2 * ROWB), m1 = ldf4(kmp + 3 * ROWB);
-            const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-            const float kmn[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-            float bias = 0.f;
-            float qp[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bias = __builtin_fmaf(qs[e], kmn[e], bias);
-                qp[e] = qs[e] * ks[e];
-            }
-#pragma unroll
-            for (int r = 0; r < 32; ++r) acc[r] = bias;
-            if constexpr (BITS == 4) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int w = i >> 1;
-                    const uint32_t ws[4] = {kc[i].x, kc[i].y, kc[i].z, kc[i].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float qa = qp[4 * (i & 1) + e];
-                        const float qb = qa * 0.0625f;
-                        const uint32_t lo = ws[e] & 0x0F0F0F0Fu, hi = ws[e] & 0xF0F0F0F0u;
-                        acc[8 * w + 0] = __builtin_fmaf(qa, cvt_ub<0>(lo), acc[8 * w + 0]);
-                        acc[8 * w + 1] = __builtin_fmaf(qb, cvt_ub<0>(hi), acc[8 * w + 1]);
-                        acc[8 * w + 2] = __builtin_fmaf(qa, cvt_ub<1>(lo), acc[8 * w + 2]);
-                        acc[8 * w + 3] = __builtin_fmaf(qb, cvt_ub<1>(hi), acc[8 * w + 3]);
-                        acc[8 * w + 4] = __builtin_fmaf(qa, cvt_ub<2>(lo), acc[8 * w + 4]);
-                        acc[8 * w + 5] = __builtin_fmaf(qb, cvt_ub<2>(hi), acc[8 * w + 5]);
-                        acc[8 * w + 6] = __builtin_fmaf(qa, cvt_ub<3>(lo), acc[8 * w + 6]);
-                        acc[8 * w + 7] = __builtin_fmaf(qb, cvt_ub<3>(hi), acc[8 * w + 7]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int w = i >> 1;
-                    const uint32_t ws[4] = {kc[i].x, kc[i].y, kc[i].z, kc[i].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float q0 = qp[4 * (i & 1) + e];
-                        const float qm[4] = {q0, q0 * 0.25f, q0 * 0.0625f, q0 * 0.015625f};
-#pragma unroll
-                        for (int mm = 0; mm < 4; ++mm) {
-                            const uint32_t part = ws[e] & (0x03030303u << (2 * mm));
-                            acc[16 * w + 0 + mm] = __builtin_fmaf(qm[mm], cvt_ub<0>(part), acc[16 * w + 0 + mm]);
-                            acc[16 * w + 4 + mm] = __builtin_fmaf(qm[mm], cvt_ub<1>(part), acc[16 * w + 4 + mm]);
-                            acc[16 * w + 8 + mm] = __builtin_fmaf(qm[mm], cvt_ub<2>(part), acc[16 * w + 8 + mm]);
-                            acc[16 * w + 12 + mm] = __builtin_fmaf(qm[mm], cvt_ub<3>(part), acc[16 * w + 12 + mm]);
-                        }
-                    }
-                }
-            }
-        }
+    // ---- scores of the keys in `acc` -> probabilities in LDS, online-softmax update
+    float pv8[8];
+    auto softmax_step = [&](float* acc, bool valid) {
         row_reduce_scatter<S>(acc);
         float sc[NT];
 #pragma unroll
@@ -216,8 +177,6 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
             if constexpr (BITS == 16) v *= p.qscale;
             sc[i] = valid ? v : -INFINITY;
         }
-
-        // ---------------- online softmax (row-uniform running max)
         float mloc = sc[0];
 #pragma unroll
         for (int i = 1; i < NT; ++i) mloc = fmaxf(mloc, sc[i]);
@@ -236,7 +195,6 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         pm *= alpha;
 #pragma unroll
         for (int c = 0; c < 32; ++c) o[c] *= alpha;
-
         // hand the probabilities to the value layout: slot (t & 3) * 8 + (t >> 2)
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
@@ -248,72 +206,173 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const float4 pa = *reinterpret_cast<const float4*>(&plds[row][tq * 8]);
         const float4 pb = *reinterpret_cast<const float4*>(&plds[row][tq * 8 + 4]);
-        const float pv8[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        pv8[0] = pa.x; pv8[1] = pa.y; pv8[2] = pa.z; pv8[3] = pa.w;
+        pv8[4] = pb.x; pv8[5] = pb.y; pv8[6] = pb.z; pv8[7] = pb.w;
+    };
 
-        // ---------------- values
-        const uint8_t* vcp = gp + (size_t)vc_row0(BITS) * ROWB + L * 16;
-        if constexpr (BITS == 16) {
+    // ---- INT-b key phase: buf rows 0..KCR-1 codes, KCR..KCR+3 (scale, min)
+    auto keys_int = [&](const uint4* buf, float* acc) {
+        const float4 s0 = as_f4(buf[KCR]), s1 = as_f4(buf[KCR + 1]);
+        const float4 m0 = as_f4(buf[KCR + 2]), m1 = as_f4(buf[KCR + 3]);
+        const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float kmn[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float bias = 0.f;
+        float qp[8];
 #pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                const uint4 c = ld16(vcp + r * ROWB);
-                const float pr = pv8[r >> 2];
-                const int cb = 8 * (r & 3);
-                const uint32_t ws[4] = {c.x, c.y, c.z, c.w};
+        for (int e = 0; e < 8; ++e) {
+            bias = __builtin_fmaf(qs[e], kmn[e], bias);
+            qp[e] = qs[e] * ks[e];
+        }
+#pragma unroll
+        for (int r = 0; r < 32; ++r) acc[r] = bias;
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int i = 0; i < KCR; ++i) {
+                const int w = i >> 1;
+                const uint32_t ws[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    o[cb + 2 * e] = __builtin_fmaf(pr, lo_h(ws[e]), o[cb + 2 * e]);
-                    o[cb + 2 * e + 1] = __builtin_fmaf(pr, hi_h(ws[e]), o[cb + 2 * e + 1]);
+                    const float qa = qp[4 * (i & 1) + e];
+                    const float qb = qa * 0.0625f;
+                    const uint32_t lo = ws[e] & 0x0F0F0F0Fu, hi = ws[e] & 0xF0F0F0F0u;
+                    acc[8 * w + 0] = __builtin_fmaf(qa, cvt_ub<0>(lo), acc[8 * w + 0]);
+                    acc[8 * w + 1] = __builtin_fmaf(qb, cvt_ub<0>(hi), acc[8 * w + 1]);
+                    acc[8 * w + 2] = __builtin_fmaf(qa, cvt_ub<1>(lo), acc[8 * w + 2]);
+                    acc[8 * w + 3] = __builtin_fmaf(qb, cvt_ub<1>(hi), acc[8 * w + 3]);
+                    acc[8 * w + 4] = __builtin_fmaf(qa, cvt_ub<2>(lo), acc[8 * w + 4]);
+                    acc[8 * w + 5] = __builtin_fmaf(qb, cvt_ub<2>(hi), acc[8 * w + 5]);
+                    acc[8 * w + 6] = __builtin_fmaf(qa, cvt_ub<3>(lo), acc[8 * w + 6]);
+                    acc[8 * w + 7] = __builtin_fmaf(qb, cvt_ub<3>(hi), acc[8 * w + 7]);
                 }
             }
         } else {
-            uint4 vc[VCR];
 #pragma unroll
-            for (int i = 0; i < VCR; ++i) vc[i] = ld16(vcp + i * ROWB);
-            const uint8_t* vmp = gp + (size_t)vm_row0(BITS) * ROWB + L * 16;
-            float4 vm[4];
+            for (int i = 0; i < KCR; ++i) {
+                const int w = i >> 1;
+                const uint32_t ws[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vm[i] = ldf4(vmp + i * ROWB);
+                for (int e = 0; e < 4; ++e) {
+                    const float q0 = qp[4 * (i & 1) + e];
+                    const float qm[4] = {q0, q0 * 0.25f, q0 * 0.0625f, q0 * 0.015625f};
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float s = (m & 1) ? vm[m >> 1].z : vm[m >> 1].x;
-                const float mn = (m & 1) ? vm[m >> 1].w : vm[m >> 1].y;
-                const float pr = pv8[m];
-                const float pv = pr * s;
-                pm = __builtin_fmaf(pr, mn, pm);
-                if constexpr (BITS == 4) {
-                    const uint32_t ws[4] = {vc[m].x, vc[m].y, vc[m].z, vc[m].w};
-                    const float pb16 = pv * 0.0625f;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const uint32_t lo = ws[u] & 0x0F0F0F0Fu, hi = ws[u] & 0xF0F0F0F0u;
-                        o[8 * u + 0] = __builtin_fmaf(pv, cvt_ub<0>(lo), o[8 * u + 0]);
-                        o[8 * u + 1] = __builtin_fmaf(pb16, cvt_ub<0>(hi), o[8 * u + 1]);
-                        o[8 * u + 2] = __builtin_fmaf(pv, cvt_ub<1>(lo), o[8 * u + 2]);
-                        o[8 * u + 3] = __builtin_fmaf(pb16, cvt_ub<1>(hi), o[8 * u + 3]);
-                        o[8 * u + 4] = __builtin_fmaf(pv, cvt_ub<2>(lo), o[8 * u + 4]);
-                        o[8 * u + 5] = __builtin_fmaf(pb16, cvt_ub<2>(hi), o[8 * u + 5]);
-                        o[8 * u + 6] = __builtin_fmaf(pv, cvt_ub<3>(lo), o[8 * u + 6]);
-                        o[8 * u + 7] = __builtin_fmaf(pb16, cvt_ub<3>(hi), o[8 * u + 7]);
-                    }
-                } else {
-                    const uint32_t w0 = (m & 1) ? vc[m >> 1].z : vc[m >> 1].x;
-                    const uint32_t w1 = (m & 1) ? vc[m >> 1].w : vc[m >> 1].y;
-                    const uint32_t ws[2] = {w0, w1};
-                    const float pvm[4] = {pv, pv * 0.25f, pv * 0.0625f, pv * 0.015625f};
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-                        for (int mm = 0; mm < 4; ++mm) {
-                            const uint32_t part = ws[u] & (0x03030303u << (2 * mm));
-                            o[16 * u + 0 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<0>(part), o[16 * u + 0 + mm]);
-                            o[16 * u + 4 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<1>(part), o[16 * u + 4 + mm]);
-                            o[16 * u + 8 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<2>(part), o[16 * u + 8 + mm]);
-                            o[16 * u + 12 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<3>(part), o[16 * u + 12 + mm]);
-                        }
+                    for (int mm = 0; mm < 4; ++mm) {
+                        const uint32_t part = ws[e] & (0x03030303u << (2 * mm));
+                        acc[16 * w + 0 + mm] = __builtin_fmaf(qm[mm], cvt_ub<0>(part), acc[16 * w + 0 + mm]);
+                        acc[16 * w + 4 + mm] = __builtin_fmaf(qm[mm], cvt_ub<1>(part), acc[16 * w + 4 + mm]);
+                        acc[16 * w + 8 + mm] = __builtin_fmaf(qm[mm], cvt_ub<2>(part), acc[16 * w + 8 + mm]);
+                        acc[16 * w + 12 + mm] = __builtin_fmaf(qm[mm], cvt_ub<3>(part), acc[16 * w + 12 + mm]);
                     }
                 }
             }
         }
+    };
+
+    // ---- INT-b value phase: buf rows 0..VCR-1 codes, VCR..VCR+3 (scale, min) pairs
+    auto values_int = [&](const uint4* buf) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float4 sm = as_f4(buf[VCR + (m >> 1)]);
+            const float s = (m & 1) ? sm.z : sm.x;
+            const float mn = (m & 1) ? sm.w : sm.y;
+            const float pr = pv8[m];
+            const float pv = pr * s;
+            pm = __builtin_fmaf(pr, mn, pm);
+            if constexpr (BITS == 4) {
+                const uint32_t ws[4] = {buf[m].x, buf[m].y, buf[m].z, buf[m].w};
+                const float pb16 = pv * 0.0625f;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t lo = ws[u] & 0x0F0F0F0Fu, hi = ws[u] & 0xF0F0F0F0u;
+                    o[8 * u + 0] = __builtin_fmaf(pv, cvt_ub<0>(lo), o[8 * u + 0]);
+                    o[8 * u + 1] = __builtin_fmaf(pb16, cvt_ub<0>(hi), o[8 * u + 1]);
+                    o[8 * u + 2] = __builtin_fmaf(pv, cvt_ub<1>(lo), o[8 * u + 2]);
+                    o[8 * u + 3] = __builtin_fmaf(pb16, cvt_ub<1>(hi), o[8 * u + 3]);
+                    o[8 * u + 4] = __builtin_fmaf(pv, cvt_ub<2>(lo), o[8 * u + 4]);
+                    o[8 * u + 5] = __builtin_fmaf(pb16, cvt_ub<2>(hi), o[8 * u + 5]);
+                    o[8 * u + 6] = __builtin_fmaf(pv, cvt_ub<3>(lo), o[8 * u + 6]);
+                    o[8 * u + 7] = __builtin_fmaf(pb16, cvt_ub<3>(hi), o[8 * u + 7]);
+                }
+            } else {
+                const uint4 c = buf[m >> 1];
+                const uint32_t ws[2] = {(m & 1) ? c.z : c.x, (m & 1) ? c.w : c.y};
+                const float pvm[4] = {pv, pv * 0.25f, pv * 0.0625f, pv * 0.015625f};
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm) {
+                        const uint32_t part = ws[u] & (0x03030303u << (2 * mm));
+                        o[16 * u + 0 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<0>(part), o[16 * u + 0 + mm]);
+                        o[16 * u + 4 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<1>(part), o[16 * u + 4 + mm]);
+                        o[16 * u + 8 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<2>(part), o[16 * u + 8 + mm]);
+                        o[16 * u + 12 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<3>(part), o[16 * u + 12 + mm]);
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- FP16 phases: 8 key rows (q . k with v_dot2) or 8 value rows
+    const half2_t qh0 = as_h2(qw[0]), qh1 = as_h2(qw[1]), qh2 = as_h2(qw[2]), qh3 = as_h2(qw[3]);
+    auto keys_fp16 = [&](const uint4* buf, float* acc) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            float a = __builtin_amdgcn_fdot2(as_h2(buf[r].x), qh0, 0.f, false);
+            a = __builtin_amdgcn_fdot2(as_h2(buf[r].y), qh1, a, false);
+            a = __builtin_amdgcn_fdot2(as_h2(buf[r].z), qh2, a, false);
+            a = __builtin_amdgcn_fdot2(as_h2(buf[r].w), qh3, a, false);
+            acc[r] = a;
+        }
+    };
+    auto values_fp16 = [&](const uint4* buf, int mbase) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float pr = pv8[mbase + (r >> 2)];
+            const int cb = 8 * (r & 3);
+            const uint32_t ws[4] = {buf[r].x, buf[r].y, buf[r].z, buf[r].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[cb + 2 * e] = __builtin_fmaf(pr, lo_h(ws[e]), o[cb + 2 * e]);
+                o[cb + 2 * e + 1] = __builtin_fmaf(pr, hi_h(ws[e]), o[cb + 2 * e + 1]);
+            }
+        }
+    };
+
+    // ---- main loop: every phase's loads are issued one phase ahead of use,
+    // into the other of two register buffers (across groups too)
+    constexpr int NPH = n_phases<BITS>();
+    uint4 bufA[NR], bufB[NR];
+    const uint8_t* gp = group_ptr(g0);
+    load_phase<BITS, D>(bufA, gp, 0, L);
+    for (int gbase = g0; gbase < g1; gbase += GPI) {
+        const bool valid = gbase + gslot < g1;
+        const bool has_next = gbase + GPI < g1;
+        const uint8_t* gn = has_next ? group_ptr(gbase + GPI) : gp;
+        float acc[32];
+#pragma unroll
+        for (int ph = 0; ph < NPH; ++ph) {
+            uint4* cur = (ph & 1) ? bufB : bufA;
+            uint4* nxt = (ph & 1) ? bufA : bufB;
+            // (on the last iteration gn == gp: the prefetch re-reads this
+            // group, a cache hit, and keeps the code free of a branch whose
+            // merge point would force the compiler to wait for every load)
+            load_phase<BITS, D>(nxt, ph + 1 < NPH ? gp : gn, ph + 1 < NPH ? ph + 1 : 0, L);
+            // keep the prefetch above this phase's arithmetic: the scheduler
+            // would otherwise sink it below the wait for `cur`
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (BITS == 16) {
+                if (ph < 4) keys_fp16(cur, acc + 8 * ph);
+                else values_fp16(cur, 2 * (ph - 4));
+                if (ph == 3) softmax_step(acc, valid);
+            } else {
+                if (ph == 0) {
+                    keys_int(cur, acc);
+                    softmax_step(acc, valid);
+                } else {
+                    values_int(cur);
+                }
+            }
+        }
+        gp = gn;
     }
 
     // ---------------- merge rows of the same head, then lanes of the same value group
@@ -348,104 +407,186 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         for (int c = 0; c < 8; ++c) o4[c] = make_float4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
         if (G == 0) *reinterpret_cast<float4*>(rec + D) = make_float4(Mx, lsum, 0.f, 0.f);
     }
+
 }
 
-__device__ __forceinline__ void tile_of(const int* nt, int x, int& k, int& j) {
-    if (x < nt[0]) { k = 0; j = x; }
-    else if (x < nt[0] + nt[1]) { k = 1; j = x - nt[0]; }
-    else { k = 2; j = x - nt[0] - nt[1]; }
+// Equal-byte split of one (sequence, KV head).  Its three segments, taken
+// in the order FP16, INT4, INT2, form one byte range of `total` bytes that
+// is cut into nw = ceil(total / per_wave) near-equal parts; part w covers
+// bytes [w*total/nw, (w+1)*total/nw).  A group block belongs to the part
+// that contains its first byte.  Every wavefront (and the combine) derives
+// the same split from seg_count, so no schedule is stored.
+struct Split {
+    int segg[3];        // group blocks in each segment
+    long long pre[3];   // first byte of each segment
+    long long total;
+    int nw;
+};
+
+template <int D>
+__device__ __forceinline__ Split split_of(const AttnParams& p, int b) {
+    Split sp;
+    const int gpc = p.C / kGroup;
+    sp.total = 0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        // chunks beyond a pool's capacity were never written: never read them
+        sp.segg[k] = min(p.seg_count[b * 3 + k], p.cap[k]) * gpc;
+        sp.pre[k] = sp.total;
+        sp.total += (long long)sp.segg[k] * (long long)group_bytes(bits_of_expert(k), D);
+    }
+    sp.nw = (int)((sp.total + p.per_wave - 1) / p.per_wave);
+    return sp;
+}
+
+// Group range [g0, g1) of segment k owned by part w.
+template <int D>
+__device__ __forceinline__ void part_groups(const Split& sp, int w, int k, int& g0, int& g1) {
+    const long long gb = (long long)group_bytes(bits_of_expert(k), D);
+    const long long o0 = (long long)w * sp.total / sp.nw - sp.pre[k];
+    const long long o1 = (long long)(w + 1) * sp.total / sp.nw - sp.pre[k];
+    long long a = o0 <= 0 ? 0 : (o0 + gb - 1) / gb;
+    long long c = o1 <= 0 ? 0 : (o1 + gb - 1) / gb;
+    g0 = (int)(a < sp.segg[k] ? a : sp.segg[k]);
+    g1 = (int)(c < sp.segg[k] ? c : sp.segg[k]);
 }
 
 }  // namespace
 
+// grid (nw_max, B*Hkv): wavefront (w, bh) streams part w of (b, h), one
+// single-bitwidth piece per segment it overlaps, and writes one partial per
+// piece at slot (w, k).
 template <int D, int HB>
-__global__ __launch_bounds__(64) void attn_tile_kernel(AttnParams p) {
-    const int x = blockIdx.x, bh = blockIdx.y;
-    int k, j;
-    tile_of(p.nt, x, k, j);
+__global__ __launch_bounds__(64, 2) void attn_tile_kernel(AttnParams p) {
+    const int w = blockIdx.x, bh = blockIdx.y;
     const int b = bh / p.Hkv;
-    // chunks beyond the pool's capacity were never written: never read them
-    const int seg_groups = min(p.seg_count[b * 3 + k], p.cap[k]) * (p.C / kGroup);
-    const int g0 = j * p.tg[k];
-    if (g0 >= seg_groups) return;
-    const int g1 = min(g0 + p.tg[k], seg_groups);
-    if (k == 0) tile_body<16, D, HB>(p, k, bh, x, g0, g1);
-    else if (k == 1) tile_body<4, D, HB>(p, k, bh, x, g0, g1);
-    else tile_body<2, D, HB>(p, k, bh, x, g0, g1);
-}
-
-// One block of D threads per (sequence, query head): thread j owns channel j.
-template <int D>
-__global__ __launch_bounds__(D) void attn_combine_kernel(CombineParams p) {
-    __shared__ float ts[4096];
-    __shared__ float qsh[D];
-    const int bq = blockIdx.x;
-    const int b = bq / p.Hq, hq = bq % p.Hq;
-    const int g = p.Hq / p.Hkv;
-    const int h = hq / g, hb = hq % g;
-    const int bh = b * p.Hkv + h;
-    const int j = threadIdx.x;
-    const int gpc = p.C / kGroup;
-    int seg_groups[3];
+    const Split sp = split_of<D>(p, b);
+    if (w >= sp.nw) return;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) seg_groups[k] = min(p.seg_count[b * 3 + k], p.cap[k]) * gpc;
-
-    float M = -INFINITY;
-    for (int x = 0; x < p.nt_total; ++x) {
-        int k, jt;
-        tile_of(p.nt, x, k, jt);
-        if (jt * p.tg[k] >= seg_groups[k]) continue;
-        const float* rec = p.part + (((size_t)bh * p.nt_total + x) * g + hb) * (D + 4);
-        M = fmaxf(M, rec[D]);
+    for (int k = 0; k < 3; ++k) {
+        int g0, g1;
+        part_groups<D>(sp, w, k, g0, g1);
+        if (g0 >= g1) continue;
+        const int slot = w * 3 + k;
+        if (k == 0) tile_body<16, D, HB>(p, k, bh, slot, g0, g1);
+        else if (k == 1) tile_body<4, D, HB>(p, k, bh, slot, g0, g1);
+        else tile_body<2, D, HB>(p, k, bh, slot, g0, g1);
     }
-    const int tl = p.tail_len;
-    if (tl > 0) {
-        qsh[j] = (float)__builtin_bit_cast(_Float16, p.q[((size_t)b * p.Hq + hq) * D + j]);
-        __syncthreads();
-        const uint16_t* tk = p.tail_k + (size_t)bh * tl * D;
-        for (int t = j; t < tl; t += D) {
-            float a = 0.f;
-            for (int c = 0; c < D; ++c) a = __builtin_fmaf(qsh[c], (float)__builtin_bit_cast(_Float16, tk[(size_t)t * D + c]), a);
-            ts[t] = a * p.qscale;
-        }
-        __syncthreads();
-        for (int t = 0; t < tl; ++t) M = fmaxf(M, ts[t]);
-    }
-    float l = 0.f, o = 0.f;
-    for (int x = 0; x < p.nt_total; ++x) {
-        int k, jt;
-        tile_of(p.nt, x, k, jt);
-        if (jt * p.tg[k] >= seg_groups[k]) continue;
-        const float* rec = p.part + (((size_t)bh * p.nt_total + x) * g + hb) * (D + 4);
-        const float w = fast_exp2(rec[D] - M);
-        l = __builtin_fmaf(w, rec[D + 1], l);
-        o = __builtin_fmaf(w, rec[j], o);
-    }
-    if (tl > 0) {
-        const uint16_t* tv = p.tail_v + (size_t)bh * tl * D;
-        for (int t = 0; t < tl; ++t) {
-            const float w = fast_exp2(ts[t] - M);
-            l += w;
-            o = __builtin_fmaf(w, (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + j]), o);
-        }
-    }
-    p.out[((size_t)b * p.Hq + hq) * D + j] = l > 0.f ? o / l : 0.f;
 }
 
-hipError_t launch_attention(const AttnParams& ap, const CombineParams& cp, int D, int HB, hipStream_t st) {
-    const dim3 grid_t(ap.nt_total, ap.B * ap.Hkv);
-    if (ap.nt_total > 0) {
-#define MKV_ATTN_CASE(DD, HH)                                                        \
-        if (D == DD && HB == HH) attn_tile_kernel<DD, HH><<<grid_t, 64, 0, st>>>(ap); \
-        else
-        MKV_ATTN_CASE(128, 1) MKV_ATTN_CASE(128, 2) MKV_ATTN_CASE(128, 4)
-        MKV_ATTN_CASE(64, 1) MKV_ATTN_CASE(64, 2) MKV_ATTN_CASE(64, 4)
-        return hipErrorInvalidValue;
-#undef MKV_ATTN_CASE
+// Merge the tile partials (and the fp16 tail) of one (sequence, KV head)
+// into the outputs of its HB query heads.  256 threads: thread (tgi, qd)
+// owns channel quad qd and walks tiles tgi, tgi + TGR, ...; every partial
+// load is independent of the others.
+template <int D, int HB>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
+    constexpr int QPR = D / 4;            // float4 quads per record
+    constexpr int TGR = 256 / QPR;        // tile groups
+    __shared__ float ts[4096];            // tail scores (log2 domain)
+    __shared__ float red[256 * 4];
+    __shared__ float lred[256];
+    __shared__ float mred[8];
+    const int bh = blockIdx.x;
+    const int b = bh / p.Hkv, h = bh % p.Hkv;
+    const int tid = threadIdx.x, qd = tid % QPR, tgi = tid / QPR;
+    const Split sp = split_of<D>(p, b);
+    // the pieces of this (b, h), in order: part w, segment k
+    const int npiece = sp.nw * 3;
+    auto piece_valid = [&](int v) {
+        int g0, g1;
+        part_groups<D>(sp, v / 3, v % 3, g0, g1);
+        return g0 < g1;
+    };
+    auto rec_of = [&](int v, int hb) {
+        return p.part + (((size_t)bh * p.nt_total + v) * HB + hb) * (D + 4);
+    };
+    for (int hb = 0; hb < HB; ++hb) {
+        const int hq = h * HB + hb;
+        // tail scores
+        if (p.tail_len > 0) {
+            const uint16_t* qp = p.q + ((size_t)b * p.Hq + hq) * D;
+            const uint16_t* tk = p.tail_k + (size_t)bh * p.tail_len * D;
+            for (int t = tid; t < p.tail_len; t += 256) {
+                float s = 0.f;
+                for (int c = 0; c < D; ++c)
+                    s = __builtin_fmaf((float)__builtin_bit_cast(_Float16, qp[c]),
+                                       (float)__builtin_bit_cast(_Float16, tk[(size_t)t * D + c]), s);
+                ts[t] = s * p.qscale;
+            }
+        }
+        // global max over tile maxima and tail scores
+        float m = -INFINITY;
+        for (int v = tid; v < npiece; v += 256)
+            if (piece_valid(v)) m = fmaxf(m, rec_of(v, hb)[D]);
+        for (int t = tid; t < p.tail_len; t += 256) m = fmaxf(m, ts[t]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if ((tid & 63) == 0) mred[tid >> 6] = m;
+        __syncthreads();
+        const float M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
+        // weighted sums
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        float lacc = 0.f;
+        if (M != -INFINITY) {
+            for (int v = tgi; v < npiece; v += TGR) {
+                if (!piece_valid(v)) continue;
+                const float* rec = rec_of(v, hb);
+                const float2 ml = *reinterpret_cast<const float2*>(rec + D);
+                const float4 o4 = *reinterpret_cast<const float4*>(rec + 4 * qd);
+                const float w = fast_exp2(ml.x - M);
+                acc.x = __builtin_fmaf(w, o4.x, acc.x);
+                acc.y = __builtin_fmaf(w, o4.y, acc.y);
+                acc.z = __builtin_fmaf(w, o4.z, acc.z);
+                acc.w = __builtin_fmaf(w, o4.w, acc.w);
+                lacc = __builtin_fmaf(w, ml.y, lacc);
+            }
+            const uint16_t* tv = p.tail_v + (size_t)bh * p.tail_len * D + 4 * qd;
+            for (int t = tgi; t < p.tail_len; t += TGR) {
+                const float w = fast_exp2(ts[t] - M);
+                acc.x = __builtin_fmaf(w, (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + 0]), acc.x);
+                acc.y = __builtin_fmaf(w, (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + 1]), acc.y);
+                acc.z = __builtin_fmaf(w, (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + 2]), acc.z);
+                acc.w = __builtin_fmaf(w, (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + 3]), acc.w);
+                lacc += w;
+            }
+        }
+        red[tid * 4 + 0] = acc.x;
+        red[tid * 4 + 1] = acc.y;
+        red[tid * 4 + 2] = acc.z;
+        red[tid * 4 + 3] = acc.w;
+        lred[tid] = lacc;
+        __syncthreads();
+        if (tid < QPR) {
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+            float l = 0.f;
+            for (int gi = 0; gi < TGR; ++gi) {
+                const int src = gi * QPR + tid;
+                o.x += red[src * 4 + 0];
+                o.y += red[src * 4 + 1];
+                o.z += red[src * 4 + 2];
+                o.w += red[src * 4 + 3];
+                l += lred[gi * QPR];
+            }
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            *reinterpret_cast<float4*>(p.out + ((size_t)b * p.Hq + hq) * D + 4 * tid) =
+                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        }
+        __syncthreads();
     }
-    const dim3 grid_c(cp.B * cp.Hq);
-    if (D == 128) attn_combine_kernel<128><<<grid_c, 128, 0, st>>>(cp);
-    else attn_combine_kernel<64><<<grid_c, 64, 0, st>>>(cp);
+}
+
+hipError_t launch_attention(const AttnParams& ap, int D, int HB, hipStream_t st) {
+    const dim3 grid(ap.nt_total / 3, ap.B * ap.Hkv);
+    const dim3 cgrid(ap.B * ap.Hkv);
+#define MKV_ATTN_CASE(DD, HH)                                                          \
+    if (D == DD && HB == HH) {                                                         \
+        if (ap.nt_total > 0) attn_tile_kernel<DD, HH><<<grid, 64, 0, st>>>(ap);        \
+        attn_combine_kernel<DD, HH><<<cgrid, 256, 0, st>>>(ap);                        \
+    } else
+    MKV_ATTN_CASE(128, 1) MKV_ATTN_CASE(128, 2) MKV_ATTN_CASE(128, 4)
+    MKV_ATTN_CASE(64, 1) MKV_ATTN_CASE(64, 2) MKV_ATTN_CASE(64, 4)
+    return hipErrorInvalidValue;
+#undef MKV_ATTN_CASE
     return hipGetLastError();
 }
 

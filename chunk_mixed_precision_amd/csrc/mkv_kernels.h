@@ -60,25 +60,14 @@ struct AttnParams {
     int cap[3];
     const int32_t* seg_count;
     int B, Hkv, Hq, C;
-    int tg[3];              // groups per tile in each pool
-    int nt[3];              // tiles per (b, h) in each pool (at capacity)
-    int nt_total;
-    float* part;            // [B*Hkv][nt_total][g][d+2]: o[d], m (log2 domain), l
-    float qscale;           // log2(e) / sqrt(d)
-};
-
-struct CombineParams {
-    const float* part;
-    const int32_t* seg_count;
-    const uint16_t* q;
-    const uint16_t* tail_k; // [B][Hkv][tail_len][d]
+    long long per_wave;     // bytes one wavefront streams (equal-byte split)
+    int nt_total;           // partial slots per (b, h): 3 * most parts of any (b, h)
+    float* part;            // [B*Hkv][nt_total][g][d+4]: o[d], m (log2 domain), l, 0, 0
+    const uint16_t* tail_k; // [B][Hkv][tail_len][d] or NULL
     const uint16_t* tail_v;
     int tail_len;
     float* out;             // [B][Hq][d]
-    int B, Hkv, Hq, C;
-    int cap[3];
-    int tg[3], nt[3], nt_total;
-    float qscale;
+    float qscale;           // log2(e) / sqrt(d)
 };
 
 // Host-side launchers (each defined next to its kernels).
@@ -86,6 +75,6 @@ hipError_t launch_router(const RouterParams& rp, hipStream_t st);
 hipError_t launch_vote(const VoteParams& vp, int n_new, hipStream_t st);
 hipError_t launch_reorder(const ReorderParams& rp, int B, hipStream_t st);
 hipError_t launch_quant(const QuantParams& qp, int D, int ngroups, hipStream_t st);
-hipError_t launch_attention(const AttnParams& ap, const CombineParams& cp, int D, int HB, hipStream_t st);
+hipError_t launch_attention(const AttnParams& ap, int D, int HB, hipStream_t st);
 
 }  // namespace mkv

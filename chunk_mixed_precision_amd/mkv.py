@@ -210,6 +210,12 @@ def quantize_pack_kv(k: torch.Tensor, v: torch.Tensor, tables: RouteTables, cach
     _check(st, "mkv_quantize_pack_kv")
 
 
+def attention_workspace(B: int, Hq: int, cache: "PackedCache", device="cuda") -> torch.Tensor:
+    """Workspace (tile partials) for mixed_kv_decode_attention."""
+    return torch.empty(workspace_bytes_attention(B, Hq, cache.Hkv, cache.d, cache.C, cache.caps),
+                       dtype=torch.uint8, device=device)
+
+
 def mixed_kv_decode_attention(q: torch.Tensor, cache: PackedCache, out: torch.Tensor = None,
                               tail_k: torch.Tensor = None, tail_v: torch.Tensor = None,
                               workspace: torch.Tensor = None, stream=None) -> torch.Tensor:
@@ -218,8 +224,7 @@ def mixed_kv_decode_attention(q: torch.Tensor, cache: PackedCache, out: torch.Te
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = torch.empty(workspace_bytes_attention(B, Hq, cache.Hkv, d, cache.C, cache.caps),
-                                dtype=torch.uint8, device=q.device)
+        workspace = attention_workspace(B, Hq, cache, q.device)
     tail_len = 0 if tail_k is None else tail_k.shape[2]
     cc = cache.c()
     st = lib().mkv_mixed_kv_decode_attention(_ptr(q), Hq, ctypes.byref(cc), _ptr(tail_k), _ptr(tail_v),

@@ -207,14 +207,17 @@ int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T,
  * over every cached token of (b, h) (all segments, in any order: attention
  * does not depend on key order) plus the tail_len fp16 tokens of the tail.
  * Cached values are dequantized in registers; accumulation is fp32.  Work
- * is split over (sequence, KV head, single-bitwidth tile of groups) and the
- * tile partials are merged with a log-sum-exp combine.
+ * is split over (sequence, KV head, single-bitwidth tile of groups) in one
+ * launch; a second launch merges the tile partials of each (sequence, KV
+ * head) with a log-sum-exp combine.
  *
  *   q_fp16      [B][Hq][d] fp16
  *   tail_k/v    [B][Hkv][tail_len][d] fp16, or NULL when tail_len == 0
  *   out         [B][Hq][d] fp32
  *   workspace   at least mkv_workspace_bytes(MKV_OP_ATTENTION, ...) bytes
- * Limits: d in {64, 128}; Hq/Hkv in {1, 2, 4, 8}; 0 <= tail_len < 4096.
+ *               (tile partials; no initial contents needed).  Calls that
+ *               overlap in time need separate workspaces.
+ * Limits: d in {64, 128}; Hq/Hkv in {1, 2, 4}; 0 <= tail_len < 4096.
  * A (b, h) with no cached token and tail_len == 0 yields zeros.
  * ---------------------------------------------------------------------- */
 int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq,

@@ -247,6 +247,21 @@ def test_determinism_bitwise():
     assert torch.equal(o1, o2)
 
 
+def test_workspace_reuse_across_calls():
+    """Repeated calls on one workspace agree bit for bit."""
+    w = configs.Workload(name="reuse", seed=81, B=2, Hq=8, Hkv=4, d=128, T=2048, C=128, mix=(0.1, 0.6, 0.3))
+    experts = synth.drawn_chunk_experts(w)
+    tab = build_tables_from_experts(experts, w.C)
+    k, v = synth.kv(w, DEV)
+    q = synth.query(w, DEV)
+    cache, out, _, _ = run_quant_attn(w, tab, k, v, q, w.n)
+    ws = mkv.attention_workspace(w.B, w.Hq, cache, DEV)
+    outs = [mkv.mixed_kv_decode_attention(q, cache, workspace=ws).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, out)
+
+
 def test_append_mode_tables():
     """Routing a new chunk at chunk_offset keeps earlier tables, never freezes
     it, and recomputes rank/perm/seg_count over all chunks."""
