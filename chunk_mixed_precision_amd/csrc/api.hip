@@ -23,9 +23,9 @@ inline int hip_status(hipError_t e) {
 // Attention work split.  The bytes of each (sequence, KV head) are cut into
 // parts of about per_wave bytes, one 64-lane wavefront per part; per_wave is
 // chosen so that the whole cache (at capacity) needs about kAttnWaves
-// wavefronts, i.e. one resident round on 256 CUs (8 per CU at the kernel's
+// wavefronts, i.e. one resident round on 256 CUs (12 per CU at the kernel's
 // register use), with a floor that keeps every wavefront busy for a while.
-constexpr long long kAttnWaves = 2048;
+constexpr long long kAttnWaves = 3072;
 constexpr long long kMinWaveBytes = 16384;
 
 inline void attn_split(int B, int Hkv, int d, const int* cap, int C, long long& per_wave, int& nt_total) {

@@ -4,8 +4,10 @@
 // segments, so every tile below has a single bitwidth and no wavefront ever
 // branches on bitwidth inside its inner loop).
 //
-// Work unit: one 64-lane wavefront = one tile = a run of group blocks
-// (32 tokens each) of one (sequence, KV head, bitwidth segment).  A wave is
+// Work: the packed bytes of each (sequence, KV head) (its FP16, INT4 and INT2
+// segments in that order) are cut into equal-byte parts, one 64-lane
+// wavefront per part; a part crossing a segment boundary is processed as one
+// single-bitwidth piece per segment, each leaving one partial.  A wave is
 // split into R = 64/S rows of S = d/8 lanes; each row handles one group
 // block per iteration (GQA: the rows of one iteration take the same group
 // for different query heads).  Inside a row, lane slot L owns channels
@@ -64,47 +66,47 @@ __device__ __forceinline__ float row_max(float v) {
     return v;
 }
 
-// Reduce-scatter of 32 per-token partial sums over the S lanes of a row.
-// On return acc[0 .. 32/S-1] hold the full sums of tokens tok_xor(S,L) ^ i.
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ float4 ldf4(const uint8_t* p) { return *reinterpret_cast<const float4*>(p); }
+
+__device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_cast(float4, u); }
+
+// Every load phase brings in 8 rows of a group block (8 x 16 B per lane).
+// INT4: 3 phases: rows 0-7 = key meta + key codes of tokens 0-15, rows 8-15 =
+//       key codes of tokens 16-31 + value meta, rows 16-23 = value codes.
+// INT2: 2 phases: key meta + key codes, value meta + value codes.
+// FP16: 8 phases: key rows 0-31, then value rows 0-31.
+template <int BITS> __host__ __device__ constexpr int n_phases() { return BITS == 16 ? 8 : (BITS == 4 ? 3 : 2); }
+
+template <int D>
+__device__ __forceinline__ void load_rows8(uint4* buf, const uint8_t* gp, int phase, int L) {
+    constexpr size_t ROWB = (size_t)(D / 8) * 16;
+    const uint8_t* src = gp + (size_t)phase * 8 * ROWB + L * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) buf[i] = ld16(src + i * ROWB);
+}
+
+// Reduce-scatter of one half (16 per-token partial sums) over the S lanes of
+// a row.  On return acc[0 .. 16/S-1] hold the full sums of tokens
+// (tok_xor(S, L) ^ i) of that half.
 template <int S>
-__device__ __forceinline__ void row_reduce_scatter(float* acc) {
+__device__ __forceinline__ void reduce_half(float* acc) {
     if constexpr (S == 16) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += dpp<kDppRowMirror>(acc[r + 16]);
+        for (int r = 0; r < 8; ++r) acc[r] += dpp<kDppRowMirror>(acc[r + 8]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += dpp<kDppRowHalfMirror>(acc[r + 4]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) acc[r] += dpp<kDppXor2>(acc[r + 2]);
+        acc[0] += dpp<kDppXor1>(acc[1]);
+    } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r) acc[r] += dpp<kDppRowHalfMirror>(acc[r + 8]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] += dpp<kDppXor2>(acc[r + 4]);
 #pragma unroll
         for (int r = 0; r < 2; ++r) acc[r] += dpp<kDppXor1>(acc[r + 2]);
-    } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += dpp<kDppRowHalfMirror>(acc[r + 16]);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) acc[r] += dpp<kDppXor2>(acc[r + 8]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += dpp<kDppXor1>(acc[r + 4]);
     }
-}
-
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ float4 ldf4(const uint8_t* p) { return *reinterpret_cast<const float4*>(p); }
-
-__device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_cast(float4, u); }
-
-// Rows of one load phase.  INT-b: phase 0 = key codes + key meta, phase 1 =
-// value codes + value meta.  FP16: eight phases of 8 rows (key rows 0-7,
-// 8-15, 16-23, 24-31, then the value rows likewise).
-template <int BITS> __host__ __device__ constexpr int ph_rows() { return BITS == 16 ? 8 : 2 * BITS + 4; }
-template <int BITS> __host__ __device__ constexpr int n_phases() { return BITS == 16 ? 8 : 2; }
-
-template <int BITS, int D>
-__device__ __forceinline__ void load_phase(uint4* buf, const uint8_t* gp, int phase, int L) {
-    constexpr int NR = ph_rows<BITS>();
-    constexpr size_t ROWB = (size_t)(D / 8) * 16;
-    const uint8_t* src = gp + (size_t)phase * NR * ROWB + L * 16;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) buf[i] = ld16(src + i * ROWB);
 }
 
 // Combine the partials of two softmax runs: (m, l, o) <- (m, l, o) + (m2, l2, o2).
@@ -120,15 +122,13 @@ __device__ __forceinline__ void merge_run(float& m, float& l, float* o, float m2
 }
 
 template <int BITS, int D, int HB>
-__device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, int x, int g0, int g1) {
+__device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, int slot, int g0, int g1) {
     constexpr int S = D / 8;
     constexpr int R = 64 / S;          // rows per wave
     constexpr int NG = D / 32;         // value groups per token
     constexpr int GPI = R / HB;        // group blocks per iteration
-    constexpr int NT = 32 / S;         // tokens per lane after the reduce-scatter
-    constexpr int KCR = kc_rows(BITS);
-    constexpr int VCR = vc_rows(BITS);
-    constexpr int NR = ph_rows<BITS>();
+    constexpr int NTH = 16 / S;        // tokens per lane and key half after the reduce-scatter
+    constexpr int NPH = n_phases<BITS>();
     constexpr size_t GB = group_bytes(BITS, D);
 
     __shared__ float plds[R][32];
@@ -153,6 +153,7 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         qs[2 * e] = lo_h(qw[e]) * p.qscale;
         qs[2 * e + 1] = hi_h(qw[e]) * p.qscale;
     }
+    const half2_t qh0 = as_h2(qw[0]), qh1 = as_h2(qw[1]), qh2 = as_h2(qw[2]), qh3 = as_h2(qw[3]);
 
     float M = -INFINITY;   // running max of this row (log2 domain), row-uniform
     float lsum = 0.f;      // this lane's share of the softmax denominator
@@ -161,33 +162,33 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
 #pragma unroll
     for (int c = 0; c < 32; ++c) o[c] = 0.f;
 
+    float sc[2 * NTH];     // this lane's key scores: half 0, then half 1
+    float pw[8];           // value weights of tokens tq + 4m (p * scale for INT-b)
+    float qp[8];           // q_j * s_j (INT-b), this group
+    float bias = 0.f;      // sum_j q_j * mn_j over this lane's channels (INT-b)
+    float acc[16];
+
     auto group_ptr = [&](int gbase) {
         const int gi = gbase + gslot;
         return seg + (size_t)(gi < g1 ? gi : g1 - 1) * GB;
     };
 
-    // ---- scores of the keys in `acc` -> probabilities in LDS, online-softmax update
-    float pv8[8];
-    auto softmax_step = [&](float* acc, bool valid) {
-        row_reduce_scatter<S>(acc);
-        float sc[NT];
+    // ---- online-softmax update from sc[], probabilities to the value layout
+    auto softmax_step = [&](bool valid) {
+        float mloc = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            float v = acc[i];
-            if constexpr (BITS == 16) v *= p.qscale;
-            sc[i] = valid ? v : -INFINITY;
+        for (int i = 0; i < 2 * NTH; ++i) {
+            if (!valid) sc[i] = -INFINITY;
+            mloc = fmaxf(mloc, sc[i]);
         }
-        float mloc = sc[0];
-#pragma unroll
-        for (int i = 1; i < NT; ++i) mloc = fmaxf(mloc, sc[i]);
         mloc = row_max<S>(mloc);
         const float Mn = fmaxf(M, mloc);
         const float alpha = (Mn == -INFINITY) ? 1.f : fast_exp2(M - Mn);
         M = Mn;
-        float pt[NT];
+        float pt[2 * NTH];
         float psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
+        for (int i = 0; i < 2 * NTH; ++i) {
             pt[i] = valid ? fast_exp2(sc[i] - Mn) : 0.f;
             psum += pt[i];
         }
@@ -195,140 +196,151 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         pm *= alpha;
 #pragma unroll
         for (int c = 0; c < 32; ++c) o[c] *= alpha;
-        // hand the probabilities to the value layout: slot (t & 3) * 8 + (t >> 2)
+        // slot of token t in the value layout: (t & 3) * 8 + (t >> 2)
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const int t = fx ^ i;
-            plds[row][(t & 3) * 8 + (t >> 2)] = pt[i];
-        }
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < NTH; ++i) {
+                const int t = 16 * hh + (fx ^ i);
+                plds[row][(t & 3) * 8 + (t >> 2)] = pt[hh * NTH + i];
+            }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const float4 pa = *reinterpret_cast<const float4*>(&plds[row][tq * 8]);
         const float4 pb = *reinterpret_cast<const float4*>(&plds[row][tq * 8 + 4]);
-        pv8[0] = pa.x; pv8[1] = pa.y; pv8[2] = pa.z; pv8[3] = pa.w;
-        pv8[4] = pb.x; pv8[5] = pb.y; pv8[6] = pb.z; pv8[7] = pb.w;
+        pw[0] = pa.x; pw[1] = pa.y; pw[2] = pa.z; pw[3] = pa.w;
+        pw[4] = pb.x; pw[5] = pb.y; pw[6] = pb.z; pw[7] = pb.w;
     };
 
-    // ---- INT-b key phase: buf rows 0..KCR-1 codes, KCR..KCR+3 (scale, min)
-    auto keys_int = [&](const uint4* buf, float* acc) {
-        const float4 s0 = as_f4(buf[KCR]), s1 = as_f4(buf[KCR + 1]);
-        const float4 m0 = as_f4(buf[KCR + 2]), m1 = as_f4(buf[KCR + 3]);
+    // ---- INT-b pieces
+    auto key_meta = [&](const uint4* m4) {           // rows: scale lo, scale hi, min lo, min hi
+        const float4 s0 = as_f4(m4[0]), s1 = as_f4(m4[1]), n0 = as_f4(m4[2]), n1 = as_f4(m4[3]);
         const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const float kmn[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        float bias = 0.f;
-        float qp[8];
+        const float kmn[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+        bias = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             bias = __builtin_fmaf(qs[e], kmn[e], bias);
             qp[e] = qs[e] * ks[e];
         }
+    };
+    auto key_half_int4 = [&](const uint4* rows) {    // 4 key-code rows of one half
 #pragma unroll
-        for (int r = 0; r < 32; ++r) acc[r] = bias;
-        if constexpr (BITS == 4) {
+        for (int r = 0; r < 16; ++r) acc[r] = bias;
 #pragma unroll
-            for (int i = 0; i < KCR; ++i) {
-                const int w = i >> 1;
-                const uint32_t ws[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+        for (int i = 0; i < 4; ++i) {
+            const int w = i >> 1;
+            const uint32_t ws[4] = {rows[i].x, rows[i].y, rows[i].z, rows[i].w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float qa = qp[4 * (i & 1) + e];
-                    const float qb = qa * 0.0625f;
-                    const uint32_t lo = ws[e] & 0x0F0F0F0Fu, hi = ws[e] & 0xF0F0F0F0u;
-                    acc[8 * w + 0] = __builtin_fmaf(qa, cvt_ub<0>(lo), acc[8 * w + 0]);
-                    acc[8 * w + 1] = __builtin_fmaf(qb, cvt_ub<0>(hi), acc[8 * w + 1]);
-                    acc[8 * w + 2] = __builtin_fmaf(qa, cvt_ub<1>(lo), acc[8 * w + 2]);
-                    acc[8 * w + 3] = __builtin_fmaf(qb, cvt_ub<1>(hi), acc[8 * w + 3]);
-                    acc[8 * w + 4] = __builtin_fmaf(qa, cvt_ub<2>(lo), acc[8 * w + 4]);
-                    acc[8 * w + 5] = __builtin_fmaf(qb, cvt_ub<2>(hi), acc[8 * w + 5]);
-                    acc[8 * w + 6] = __builtin_fmaf(qa, cvt_ub<3>(lo), acc[8 * w + 6]);
-                    acc[8 * w + 7] = __builtin_fmaf(qb, cvt_ub<3>(hi), acc[8 * w + 7]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                const float qa = qp[4 * (i & 1) + e];
+                const float qb = qa * 0.0625f;
+                const uint32_t lo = ws[e] & 0x0F0F0F0Fu, hi = ws[e] & 0xF0F0F0F0u;
+                acc[8 * w + 0] = __builtin_fmaf(qa, cvt_ub<0>(lo), acc[8 * w + 0]);
+                acc[8 * w + 1] = __builtin_fmaf(qb, cvt_ub<0>(hi), acc[8 * w + 1]);
+                acc[8 * w + 2] = __builtin_fmaf(qa, cvt_ub<1>(lo), acc[8 * w + 2]);
+                acc[8 * w + 3] = __builtin_fmaf(qb, cvt_ub<1>(hi), acc[8 * w + 3]);
+                acc[8 * w + 4] = __builtin_fmaf(qa, cvt_ub<2>(lo), acc[8 * w + 4]);
+                acc[8 * w + 5] = __builtin_fmaf(qb, cvt_ub<2>(hi), acc[8 * w + 5]);
+                acc[8 * w + 6] = __builtin_fmaf(qa, cvt_ub<3>(lo), acc[8 * w + 6]);
+                acc[8 * w + 7] = __builtin_fmaf(qb, cvt_ub<3>(hi), acc[8 * w + 7]);
             }
-        } else {
+        }
+    };
+    auto key_half_int2 = [&](const uint4* rows) {    // 2 key-code rows of one half
 #pragma unroll
-            for (int i = 0; i < KCR; ++i) {
-                const int w = i >> 1;
-                const uint32_t ws[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+        for (int r = 0; r < 16; ++r) acc[r] = bias;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float q0 = qp[4 * (i & 1) + e];
-                    const float qm[4] = {q0, q0 * 0.25f, q0 * 0.0625f, q0 * 0.015625f};
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t ws[4] = {rows[i].x, rows[i].y, rows[i].z, rows[i].w};
 #pragma unroll
-                    for (int mm = 0; mm < 4; ++mm) {
-                        const uint32_t part = ws[e] & (0x03030303u << (2 * mm));
-                        acc[16 * w + 0 + mm] = __builtin_fmaf(qm[mm], cvt_ub<0>(part), acc[16 * w + 0 + mm]);
-                        acc[16 * w + 4 + mm] = __builtin_fmaf(qm[mm], cvt_ub<1>(part), acc[16 * w + 4 + mm]);
-                        acc[16 * w + 8 + mm] = __builtin_fmaf(qm[mm], cvt_ub<2>(part), acc[16 * w + 8 + mm]);
-                        acc[16 * w + 12 + mm] = __builtin_fmaf(qm[mm], cvt_ub<3>(part), acc[16 * w + 12 + mm]);
-                    }
+            for (int e = 0; e < 4; ++e) {
+                const float q0 = qp[4 * i + e];
+                const float qm[4] = {q0, q0 * 0.25f, q0 * 0.0625f, q0 * 0.015625f};
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const uint32_t part = ws[e] & (0x03030303u << (2 * mm));
+                    acc[0 + mm] = __builtin_fmaf(qm[mm], cvt_ub<0>(part), acc[0 + mm]);
+                    acc[4 + mm] = __builtin_fmaf(qm[mm], cvt_ub<1>(part), acc[4 + mm]);
+                    acc[8 + mm] = __builtin_fmaf(qm[mm], cvt_ub<2>(part), acc[8 + mm]);
+                    acc[12 + mm] = __builtin_fmaf(qm[mm], cvt_ub<3>(part), acc[12 + mm]);
                 }
             }
         }
     };
-
-    // ---- INT-b value phase: buf rows 0..VCR-1 codes, VCR..VCR+3 (scale, min) pairs
-    auto values_int = [&](const uint4* buf) {
+    auto take_half = [&](int hh) {
+        reduce_half<S>(acc);
+#pragma unroll
+        for (int i = 0; i < NTH; ++i) sc[hh * NTH + i] = acc[i];
+    };
+    auto value_meta = [&](const uint4* m4) {         // (scale, min) of tokens t_{2r}, t_{2r+1}
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            const float4 sm = as_f4(buf[VCR + (m >> 1)]);
+            const float4 sm = as_f4(m4[m >> 1]);
             const float s = (m & 1) ? sm.z : sm.x;
             const float mn = (m & 1) ? sm.w : sm.y;
-            const float pr = pv8[m];
-            const float pv = pr * s;
-            pm = __builtin_fmaf(pr, mn, pm);
-            if constexpr (BITS == 4) {
-                const uint32_t ws[4] = {buf[m].x, buf[m].y, buf[m].z, buf[m].w};
-                const float pb16 = pv * 0.0625f;
+            pm = __builtin_fmaf(pw[m], mn, pm);
+            pw[m] *= s;
+        }
+    };
+    auto values_int4 = [&](const uint4* rows) {      // row m: token tq + 4m
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t lo = ws[u] & 0x0F0F0F0Fu, hi = ws[u] & 0xF0F0F0F0u;
-                    o[8 * u + 0] = __builtin_fmaf(pv, cvt_ub<0>(lo), o[8 * u + 0]);
-                    o[8 * u + 1] = __builtin_fmaf(pb16, cvt_ub<0>(hi), o[8 * u + 1]);
-                    o[8 * u + 2] = __builtin_fmaf(pv, cvt_ub<1>(lo), o[8 * u + 2]);
-                    o[8 * u + 3] = __builtin_fmaf(pb16, cvt_ub<1>(hi), o[8 * u + 3]);
-                    o[8 * u + 4] = __builtin_fmaf(pv, cvt_ub<2>(lo), o[8 * u + 4]);
-                    o[8 * u + 5] = __builtin_fmaf(pb16, cvt_ub<2>(hi), o[8 * u + 5]);
-                    o[8 * u + 6] = __builtin_fmaf(pv, cvt_ub<3>(lo), o[8 * u + 6]);
-                    o[8 * u + 7] = __builtin_fmaf(pb16, cvt_ub<3>(hi), o[8 * u + 7]);
-                }
-            } else {
-                const uint4 c = buf[m >> 1];
-                const uint32_t ws[2] = {(m & 1) ? c.z : c.x, (m & 1) ? c.w : c.y};
-                const float pvm[4] = {pv, pv * 0.25f, pv * 0.0625f, pv * 0.015625f};
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t ws[4] = {rows[m].x, rows[m].y, rows[m].z, rows[m].w};
+            const float pv = pw[m], pb16 = pv * 0.0625f;
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t lo = ws[u] & 0x0F0F0F0Fu, hi = ws[u] & 0xF0F0F0F0u;
+                o[8 * u + 0] = __builtin_fmaf(pv, cvt_ub<0>(lo), o[8 * u + 0]);
+                o[8 * u + 1] = __builtin_fmaf(pb16, cvt_ub<0>(hi), o[8 * u + 1]);
+                o[8 * u + 2] = __builtin_fmaf(pv, cvt_ub<1>(lo), o[8 * u + 2]);
+                o[8 * u + 3] = __builtin_fmaf(pb16, cvt_ub<1>(hi), o[8 * u + 3]);
+                o[8 * u + 4] = __builtin_fmaf(pv, cvt_ub<2>(lo), o[8 * u + 4]);
+                o[8 * u + 5] = __builtin_fmaf(pb16, cvt_ub<2>(hi), o[8 * u + 5]);
+                o[8 * u + 6] = __builtin_fmaf(pv, cvt_ub<3>(lo), o[8 * u + 6]);
+                o[8 * u + 7] = __builtin_fmaf(pb16, cvt_ub<3>(hi), o[8 * u + 7]);
+            }
+        }
+    };
+    auto values_int2 = [&](const uint4* rows) {      // row r: tokens t_{2r} (dwords 0,1), t_{2r+1} (2,3)
 #pragma unroll
-                    for (int mm = 0; mm < 4; ++mm) {
-                        const uint32_t part = ws[u] & (0x03030303u << (2 * mm));
-                        o[16 * u + 0 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<0>(part), o[16 * u + 0 + mm]);
-                        o[16 * u + 4 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<1>(part), o[16 * u + 4 + mm]);
-                        o[16 * u + 8 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<2>(part), o[16 * u + 8 + mm]);
-                        o[16 * u + 12 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<3>(part), o[16 * u + 12 + mm]);
-                    }
+        for (int m = 0; m < 8; ++m) {
+            const uint4 c = rows[m >> 1];
+            const uint32_t ws[2] = {(m & 1) ? c.z : c.x, (m & 1) ? c.w : c.y};
+            const float pv = pw[m];
+            const float pvm[4] = {pv, pv * 0.25f, pv * 0.0625f, pv * 0.015625f};
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const uint32_t part = ws[u] & (0x03030303u << (2 * mm));
+                    o[16 * u + 0 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<0>(part), o[16 * u + 0 + mm]);
+                    o[16 * u + 4 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<1>(part), o[16 * u + 4 + mm]);
+                    o[16 * u + 8 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<2>(part), o[16 * u + 8 + mm]);
+                    o[16 * u + 12 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<3>(part), o[16 * u + 12 + mm]);
                 }
             }
         }
     };
 
-    // ---- FP16 phases: 8 key rows (q . k with v_dot2) or 8 value rows
-    const half2_t qh0 = as_h2(qw[0]), qh1 = as_h2(qw[1]), qh2 = as_h2(qw[2]), qh3 = as_h2(qw[3]);
-    auto keys_fp16 = [&](const uint4* buf, float* acc) {
+    // ---- FP16 pieces: 8 key rows (q . k with v_dot2) or 8 value rows
+    auto keys_fp16 = [&](const uint4* rows, int r0) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            float a = __builtin_amdgcn_fdot2(as_h2(buf[r].x), qh0, 0.f, false);
-            a = __builtin_amdgcn_fdot2(as_h2(buf[r].y), qh1, a, false);
-            a = __builtin_amdgcn_fdot2(as_h2(buf[r].z), qh2, a, false);
-            a = __builtin_amdgcn_fdot2(as_h2(buf[r].w), qh3, a, false);
-            acc[r] = a;
+            float a = __builtin_amdgcn_fdot2(as_h2(rows[r].x), qh0, 0.f, false);
+            a = __builtin_amdgcn_fdot2(as_h2(rows[r].y), qh1, a, false);
+            a = __builtin_amdgcn_fdot2(as_h2(rows[r].z), qh2, a, false);
+            a = __builtin_amdgcn_fdot2(as_h2(rows[r].w), qh3, a, false);
+            acc[r0 + r] = a;
         }
     };
-    auto values_fp16 = [&](const uint4* buf, int mbase) {
+    auto values_fp16 = [&](const uint4* rows, int mbase) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float pr = pv8[mbase + (r >> 2)];
+            const float pr = pw[mbase + (r >> 2)];
             const int cb = 8 * (r & 3);
-            const uint32_t ws[4] = {buf[r].x, buf[r].y, buf[r].z, buf[r].w};
+            const uint32_t ws[4] = {rows[r].x, rows[r].y, rows[r].z, rows[r].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 o[cb + 2 * e] = __builtin_fmaf(pr, lo_h(ws[e]), o[cb + 2 * e]);
@@ -337,42 +349,89 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         }
     };
 
-    // ---- main loop: every phase's loads are issued one phase ahead of use,
-    // into the other of two register buffers (across groups too)
-    constexpr int NPH = n_phases<BITS>();
-    uint4 bufA[NR], bufB[NR];
-    const uint8_t* gp = group_ptr(g0);
-    load_phase<BITS, D>(bufA, gp, 0, L);
-    for (int gbase = g0; gbase < g1; gbase += GPI) {
-        const bool valid = gbase + gslot < g1;
-        const bool has_next = gbase + GPI < g1;
-        const uint8_t* gn = has_next ? group_ptr(gbase + GPI) : gp;
-        float acc[32];
-#pragma unroll
-        for (int ph = 0; ph < NPH; ++ph) {
-            uint4* cur = (ph & 1) ? bufB : bufA;
-            uint4* nxt = (ph & 1) ? bufA : bufB;
-            // (on the last iteration gn == gp: the prefetch re-reads this
-            // group, a cache hit, and keeps the code free of a branch whose
-            // merge point would force the compiler to wait for every load)
-            load_phase<BITS, D>(nxt, ph + 1 < NPH ? gp : gn, ph + 1 < NPH ? ph + 1 : 0, L);
-            // keep the prefetch above this phase's arithmetic: the scheduler
-            // would otherwise sink it below the wait for `cur`
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (BITS == 16) {
-                if (ph < 4) keys_fp16(cur, acc + 8 * ph);
-                else values_fp16(cur, 2 * (ph - 4));
-                if (ph == 3) softmax_step(acc, valid);
+    // one phase's arithmetic on the rows in `cur`
+    auto compute_phase = [&](int ph, const uint4* cur, bool valid) {
+        if constexpr (BITS == 4) {
+            if (ph == 0) {
+                key_meta(cur);
+                key_half_int4(cur + 4);
+                take_half(0);
+            } else if (ph == 1) {
+                key_half_int4(cur);
+                take_half(1);
+                softmax_step(valid);
+                value_meta(cur + 4);
             } else {
-                if (ph == 0) {
-                    keys_int(cur, acc);
-                    softmax_step(acc, valid);
-                } else {
-                    values_int(cur);
+                values_int4(cur);
+            }
+        } else if constexpr (BITS == 2) {
+            if (ph == 0) {
+                key_meta(cur);
+                key_half_int2(cur + 4);
+                take_half(0);
+                key_half_int2(cur + 6);
+                take_half(1);
+                softmax_step(valid);
+            } else {
+                value_meta(cur);
+                values_int2(cur + 4);
+            }
+        } else {
+            if (ph < 4) {
+                keys_fp16(cur, 8 * (ph & 1));
+                if (ph & 1) {
+                    take_half(ph >> 1);
+                    if (ph == 3) {
+#pragma unroll
+                        for (int i = 0; i < 2 * NTH; ++i) sc[i] *= p.qscale;
+                        softmax_step(valid);
+                    }
                 }
+            } else {
+                values_fp16(cur, 2 * (ph - 4));
             }
         }
-        gp = gn;
+    };
+
+    // ---- main loop.  Every phase's loads are issued one phase ahead, into
+    // the other of two 8-row register buffers; the last phase of a group
+    // prefetches the next group's first phase (or, at the end, re-reads this
+    // group: a cache hit that keeps the loop free of a branch whose merge
+    // point would make the compiler wait for every outstanding load).
+    uint4 bufA[8], bufB[8];
+    auto run_group = [&](auto par_tag, int gbase, const uint8_t* gp, const uint8_t* gn) {
+        constexpr int PAR = decltype(par_tag)::value;
+        const bool valid = gbase + gslot < g1;
+#pragma unroll
+        for (int ph = 0; ph < NPH; ++ph) {
+            uint4* cur = ((ph + PAR) & 1) ? bufB : bufA;
+            uint4* nxt = ((ph + PAR) & 1) ? bufA : bufB;
+            load_rows8<D>(nxt, ph + 1 < NPH ? gp : gn, ph + 1 < NPH ? ph + 1 : 0, L);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_phase(ph, cur, valid);
+        }
+    };
+    const uint8_t* gp = group_ptr(g0);
+    load_rows8<D>(bufA, gp, 0, L);
+    if constexpr (NPH % 2 == 0) {
+        for (int gbase = g0; gbase < g1; gbase += GPI) {
+            const uint8_t* gn = gbase + GPI < g1 ? group_ptr(gbase + GPI) : gp;
+            run_group(std::integral_constant<int, 0>{}, gbase, gp, gn);
+            gp = gn;
+        }
+    } else {
+        // odd phase count: buffer parity flips every group, so groups go in pairs
+        for (int gbase = g0; gbase < g1; gbase += 2 * GPI) {
+            const uint8_t* gn = gbase + GPI < g1 ? group_ptr(gbase + GPI) : gp;
+            run_group(std::integral_constant<int, 0>{}, gbase, gp, gn);
+            if (gbase + GPI < g1) {
+                const uint8_t* gn2 = gbase + 2 * GPI < g1 ? group_ptr(gbase + 2 * GPI) : gn;
+                run_group(std::integral_constant<int, 1>{}, gbase + GPI, gn, gn2);
+                gp = gn2;
+            } else {
+                gp = gn;
+            }
+        }
     }
 
     // ---------------- merge rows of the same head, then lanes of the same value group
@@ -383,10 +442,10 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
     float Mx = M;
 #pragma unroll
     for (int off = S * HB; off < 64; off <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, off));
-    const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mx);
-    lsum *= sc;
+    const float rs = (M == -INFINITY) ? 0.f : fast_exp2(M - Mx);
+    lsum *= rs;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] *= sc;
+    for (int c = 0; c < 32; ++c) o[c] *= rs;
 #pragma unroll
     for (int off = 1; off < S; off <<= 1) lsum += __shfl_xor(lsum, off);
 #pragma unroll
@@ -401,7 +460,7 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         o[c] = v;
     }
     if (row == hb && tq == 0) {
-        float* rec = p.part + (((size_t)bh * p.nt_total + x) * HB + hb) * (D + 4);
+        float* rec = p.part + (((size_t)bh * p.nt_total + slot) * HB + hb) * (D + 4);
         float4* o4 = reinterpret_cast<float4*>(rec + 32 * G);
 #pragma unroll
         for (int c = 0; c < 8; ++c) o4[c] = make_float4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
@@ -457,7 +516,7 @@ __device__ __forceinline__ void part_groups(const Split& sp, int w, int k, int& 
 // single-bitwidth piece per segment it overlaps, and writes one partial per
 // piece at slot (w, k).
 template <int D, int HB>
-__global__ __launch_bounds__(64, 2) void attn_tile_kernel(AttnParams p) {
+__global__ __launch_bounds__(64, 3) void attn_tile_kernel(AttnParams p) {
     const int w = blockIdx.x, bh = blockIdx.y;
     const int b = bh / p.Hkv;
     const Split sp = split_of<D>(p, b);
@@ -466,110 +525,100 @@ __global__ __launch_bounds__(64, 2) void attn_tile_kernel(AttnParams p) {
     for (int k = 0; k < 3; ++k) {
         int g0, g1;
         part_groups<D>(sp, w, k, g0, g1);
-        if (g0 >= g1) continue;
         const int slot = w * 3 + k;
+        if (g0 >= g1) {
+            // empty piece: mark it so the combine skips it
+            if (threadIdx.x < HB) {
+                float* rec = p.part + (((size_t)bh * p.nt_total + slot) * HB + threadIdx.x) * (D + 4);
+                *reinterpret_cast<float4*>(rec + D) = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+            }
+            continue;
+        }
         if (k == 0) tile_body<16, D, HB>(p, k, bh, slot, g0, g1);
         else if (k == 1) tile_body<4, D, HB>(p, k, bh, slot, g0, g1);
         else tile_body<2, D, HB>(p, k, bh, slot, g0, g1);
     }
 }
 
-// Merge the tile partials (and the fp16 tail) of one (sequence, KV head)
-// into the outputs of its HB query heads.  256 threads: thread (tgi, qd)
-// owns channel quad qd and walks tiles tgi, tgi + TGR, ...; every partial
-// load is independent of the others.
+// Merge the piece partials (and the fp16 tail) of one (sequence, KV head)
+// into the outputs of its HB query heads.  512 threads: thread (tgi, qd)
+// owns channel quad qd and merges pieces tgi, tgi + TGR, ... online, with
+// its loads batched so that they are in flight together; a piece without
+// group blocks carries m = -inf and is skipped.
 template <int D, int HB>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
+__global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
+    constexpr int NT = 512;
     constexpr int QPR = D / 4;            // float4 quads per record
-    constexpr int TGR = 256 / QPR;        // tile groups
+    constexpr int TGR = NT / QPR;         // piece groups
+    constexpr int BATCH = 4;
     __shared__ float ts[4096];            // tail scores (log2 domain)
-    __shared__ float red[256 * 4];
-    __shared__ float lred[256];
-    __shared__ float mred[8];
+    __shared__ float4 red_o[NT];
+    __shared__ float2 red_ml[NT];
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv, h = bh % p.Hkv;
     const int tid = threadIdx.x, qd = tid % QPR, tgi = tid / QPR;
-    const Split sp = split_of<D>(p, b);
-    // the pieces of this (b, h), in order: part w, segment k
-    const int npiece = sp.nw * 3;
-    auto piece_valid = [&](int v) {
-        int g0, g1;
-        part_groups<D>(sp, v / 3, v % 3, g0, g1);
-        return g0 < g1;
-    };
+    const int npiece = split_of<D>(p, b).nw * 3;
     auto rec_of = [&](int v, int hb) {
         return p.part + (((size_t)bh * p.nt_total + v) * HB + hb) * (D + 4);
     };
     for (int hb = 0; hb < HB; ++hb) {
         const int hq = h * HB + hb;
-        // tail scores
         if (p.tail_len > 0) {
             const uint16_t* qp = p.q + ((size_t)b * p.Hq + hq) * D;
             const uint16_t* tk = p.tail_k + (size_t)bh * p.tail_len * D;
-            for (int t = tid; t < p.tail_len; t += 256) {
+            for (int t = tid; t < p.tail_len; t += NT) {
                 float s = 0.f;
                 for (int c = 0; c < D; ++c)
                     s = __builtin_fmaf((float)__builtin_bit_cast(_Float16, qp[c]),
                                        (float)__builtin_bit_cast(_Float16, tk[(size_t)t * D + c]), s);
                 ts[t] = s * p.qscale;
             }
+            __syncthreads();
         }
-        // global max over tile maxima and tail scores
-        float m = -INFINITY;
-        for (int v = tid; v < npiece; v += 256)
-            if (piece_valid(v)) m = fmaxf(m, rec_of(v, hb)[D]);
-        for (int t = tid; t < p.tail_len; t += 256) m = fmaxf(m, ts[t]);
+        float m = -INFINITY, l = 0.f;
+        float o[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int v0 = tgi; v0 < npiece; v0 += TGR * BATCH) {
+            float2 ml[BATCH];
+            float4 ov[BATCH];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        if ((tid & 63) == 0) mred[tid >> 6] = m;
-        __syncthreads();
-        const float M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
-        // weighted sums
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        float lacc = 0.f;
-        if (M != -INFINITY) {
-            for (int v = tgi; v < npiece; v += TGR) {
-                if (!piece_valid(v)) continue;
-                const float* rec = rec_of(v, hb);
-                const float2 ml = *reinterpret_cast<const float2*>(rec + D);
-                const float4 o4 = *reinterpret_cast<const float4*>(rec + 4 * qd);
-                const float w = fast_exp2(ml.x - M);
-                acc.x = __builtin_fmaf(w, o4.x, acc.x);
-                acc.y = __builtin_fmaf(w, o4.y, acc.y);
-                acc.z = __builtin_fmaf(w, o4.z, acc.z);
-                acc.w = __builtin_fmaf(w, o4.w, acc.w);
-                lacc = __builtin_fmaf(w, ml.y, lacc);
+            for (int j = 0; j < BATCH; ++j) {
+                const int v = v0 + j * TGR;
+                const float* rec = rec_of(v < npiece ? v : v0, hb);
+                ml[j] = *reinterpret_cast<const float2*>(rec + D);
+                ov[j] = *reinterpret_cast<const float4*>(rec + 4 * qd);
+                if (v >= npiece) ml[j].x = -INFINITY;
             }
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                if (ml[j].x == -INFINITY) continue;
+                const float o2[4] = {ov[j].x, ov[j].y, ov[j].z, ov[j].w};
+                merge_run<4>(m, l, o, ml[j].x, ml[j].y, o2);
+            }
+        }
+        if (p.tail_len > 0) {
             const uint16_t* tv = p.tail_v + (size_t)bh * p.tail_len * D + 4 * qd;
             for (int t = tgi; t < p.tail_len; t += TGR) {
-                const float w = fast_exp2(ts[t] - M);
-                acc.x = __builtin_fmaf(w, (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + 0]), acc.x);
-                acc.y = __builtin_fmaf(w, (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + 1]), acc.y);
-                acc.z = __builtin_fmaf(w, (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + 2]), acc.z);
-                acc.w = __builtin_fmaf(w, (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + 3]), acc.w);
-                lacc += w;
+                float vf[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) vf[c] = (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + c]);
+                merge_run<4>(m, l, o, ts[t], 1.f, vf);
             }
         }
-        red[tid * 4 + 0] = acc.x;
-        red[tid * 4 + 1] = acc.y;
-        red[tid * 4 + 2] = acc.z;
-        red[tid * 4 + 3] = acc.w;
-        lred[tid] = lacc;
+        red_o[tid] = make_float4(o[0], o[1], o[2], o[3]);
+        red_ml[tid] = make_float2(m, l);
         __syncthreads();
         if (tid < QPR) {
-            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-            float l = 0.f;
+            float mm = -INFINITY, ll = 0.f;
+            float oo[4] = {0.f, 0.f, 0.f, 0.f};
             for (int gi = 0; gi < TGR; ++gi) {
-                const int src = gi * QPR + tid;
-                o.x += red[src * 4 + 0];
-                o.y += red[src * 4 + 1];
-                o.z += red[src * 4 + 2];
-                o.w += red[src * 4 + 3];
-                l += lred[gi * QPR];
+                const float4 x = red_o[gi * QPR + tid];
+                const float2 y = red_ml[gi * QPR + tid];
+                const float o2[4] = {x.x, x.y, x.z, x.w};
+                merge_run<4>(mm, ll, oo, y.x, y.y, o2);
             }
-            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float inv = ll > 0.f ? 1.f / ll : 0.f;
             *reinterpret_cast<float4*>(p.out + ((size_t)b * p.Hq + hq) * D + 4 * tid) =
-                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+                make_float4(oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv);
         }
         __syncthreads();
     }
@@ -581,7 +630,7 @@ hipError_t launch_attention(const AttnParams& ap, int D, int HB, hipStream_t st)
 #define MKV_ATTN_CASE(DD, HH)                                                          \
     if (D == DD && HB == HH) {                                                         \
         if (ap.nt_total > 0) attn_tile_kernel<DD, HH><<<grid, 64, 0, st>>>(ap);        \
-        attn_combine_kernel<DD, HH><<<cgrid, 256, 0, st>>>(ap);                        \
+        attn_combine_kernel<DD, HH><<<cgrid, 512, 0, st>>>(ap);                        \
     } else
     MKV_ATTN_CASE(128, 1) MKV_ATTN_CASE(128, 2) MKV_ATTN_CASE(128, 4)
     MKV_ATTN_CASE(64, 1) MKV_ATTN_CASE(64, 2) MKV_ATTN_CASE(64, 4)

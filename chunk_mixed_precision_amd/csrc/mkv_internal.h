@@ -16,17 +16,16 @@ __host__ __device__ constexpr int bits_of_expert(int k) { return k == 0 ? 16 : (
 __host__ __device__ constexpr int expert_of_bits(int b) { return b == 16 ? 0 : (b == 4 ? 1 : (b == 2 ? 2 : -1)); }
 
 // Rows (of S 16-byte cells) in each section of a group block.
+// INT-b: [key meta 4][key codes 2b][value meta 4][value codes 2b]
+// FP16:  [keys 32][values 32]
 __host__ __device__ constexpr int kc_rows(int bits) { return bits == 16 ? 32 : 2 * bits; }
-__host__ __device__ constexpr int km_rows(int bits) { return bits == 16 ? 0 : 4; }
 __host__ __device__ constexpr int vc_rows(int bits) { return bits == 16 ? 32 : 2 * bits; }
-__host__ __device__ constexpr int vm_rows(int bits) { return bits == 16 ? 0 : 4; }
-__host__ __device__ constexpr int group_rows(int bits) {
-    return kc_rows(bits) + km_rows(bits) + vc_rows(bits) + vm_rows(bits);
-}
-// Row offsets of the sections.
-__host__ __device__ constexpr int km_row0(int bits) { return kc_rows(bits); }
-__host__ __device__ constexpr int vc_row0(int bits) { return kc_rows(bits) + km_rows(bits); }
-__host__ __device__ constexpr int vm_row0(int bits) { return kc_rows(bits) + km_rows(bits) + vc_rows(bits); }
+__host__ __device__ constexpr int meta_rows(int bits) { return bits == 16 ? 0 : 4; }
+__host__ __device__ constexpr int group_rows(int bits) { return kc_rows(bits) + vc_rows(bits) + 2 * meta_rows(bits); }
+__host__ __device__ constexpr int km_row0(int bits) { return 0; }
+__host__ __device__ constexpr int kc_row0(int bits) { return meta_rows(bits); }
+__host__ __device__ constexpr int vm_row0(int bits) { return meta_rows(bits) + kc_rows(bits); }
+__host__ __device__ constexpr int vc_row0(int bits) { return 2 * meta_rows(bits) + kc_rows(bits); }
 
 __host__ __device__ constexpr int lane_slots(int d) { return d / 8; }
 __host__ __device__ constexpr size_t group_bytes(int bits, int d) {
@@ -34,14 +33,18 @@ __host__ __device__ constexpr size_t group_bytes(int bits, int d) {
 }
 
 // Token permutation of the key rows/fields of lane slot L (S = d/8 slots).
-// Field position r of lane slot L holds token r ^ tok_xor(S, L).  The xor
-// masks make the reduce-scatter of the q.k partial sums over the S lanes of
-// a row select-free: at each butterfly step every lane keeps the low half of
-// its registers and its partner's high half holds the same tokens.
+// Field position r (0..31) of lane slot L holds token tok_of(S, L, r): the
+// two halves r < 16 and r >= 16 keep their tokens (0..15 and 16..31) and
+// inside a half the position is xor-ed with tok_xor(S, L).  The xor masks
+// make the reduce-scatter of the q.k partial sums of one half over the S
+// lanes of a row select-free: at every butterfly step each lane keeps the
+// low half of its registers and its DPP partner's high half holds the same
+// tokens.
 __host__ __device__ constexpr int tok_xor(int S, int L) {
-    return S == 16 ? ((((L >> 3) & 1) * 24) ^ (((L >> 2) & 1) * 14) ^ (((L >> 1) & 1) * 4) ^ ((L & 1) * 2))
-                   : ((((L >> 2) & 1) * 28) ^ (((L >> 1) & 1) * 8) ^ ((L & 1) * 4));
+    return S == 16 ? ((L & 1) * 1) ^ (((L >> 1) & 1) * 2) ^ (((L >> 2) & 1) * 7) ^ (((L >> 3) & 1) * 12)
+                   : ((L & 1) * 2) ^ (((L >> 1) & 1) * 4) ^ (((L >> 2) & 1) * 14);
 }
+__host__ __device__ constexpr int tok_of(int S, int L, int r) { return (r & 16) | ((r & 15) ^ tok_xor(S, L)); }
 
 // Values: lane slot L covers value group G = L % NG and tokens tq + 4m,
 // tq = L / NG, m = 0..7 (NG = d/32).

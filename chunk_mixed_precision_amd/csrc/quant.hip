@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64) void quant_pack_kernel(QuantParams p) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int t = tr + TPI * i;
-            const int kr = t ^ tok_xor(S, ls);
+            const int kr = tok_of(S, ls, t);
             *reinterpret_cast<uint4*>(dst + ((size_t)kr * S + ls) * 16) = kcell[i];
             const int vr = ((t >> 2) << 2) | (ls & 3);
             const int vl = vslot_of(t & 3, ls >> 2, NG);
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64) void quant_pack_kernel(QuantParams p) {
                 kc_lds[8 * ls + e][t] = (uint8_t)code_of<BITS>(kf[i][e], kmn[e], kr[e], kz[e]);
         }
         if (tr == 0) {
-            float4* km = reinterpret_cast<float4*>(dst + (size_t)km_row0(BITS) * S * 16);
+            float4* km = reinterpret_cast<float4*>(dst + (size_t)km_row0(BITS) * S * 16);  // key meta rows
             km[0 * S + ls] = make_float4(ks[0], ks[1], ks[2], ks[3]);
             km[1 * S + ls] = make_float4(ks[4], ks[5], ks[6], ks[7]);
             km[2 * S + ls] = make_float4(kmn[0], kmn[1], kmn[2], kmn[3]);
@@ -189,20 +189,20 @@ __global__ __launch_bounds__(64) void quant_pack_kernel(QuantParams p) {
         __syncthreads();
         // ---------------- key code cells: gather from LDS in the reader's order
         constexpr int KCR = kc_rows(BITS);
+        uint8_t* kcd = dst + (size_t)kc_row0(BITS) * S * 16;
         for (int c = lane; c < KCR * S; c += 64) {
             const int row = c / S, L = c % S;
             const int w = row >> 1;
-            const int fx = tok_xor(S, L);
             uint32_t words[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 8 * L + 4 * (row & 1) + e;
                 uint32_t acc = 0;
 #pragma unroll
-                for (int i = 0; i < F; ++i) acc |= (uint32_t)kc_lds[j][(F * w + i) ^ fx] << (BITS * i);
+                for (int i = 0; i < F; ++i) acc |= (uint32_t)kc_lds[j][tok_of(S, L, F * w + i)] << (BITS * i);
                 words[e] = acc;
             }
-            *reinterpret_cast<uint4*>(dst + ((size_t)row * S + L) * 16) = make_uint4(words[0], words[1], words[2], words[3]);
+            *reinterpret_cast<uint4*>(kcd + ((size_t)row * S + L) * 16) = make_uint4(words[0], words[1], words[2], words[3]);
         }
     };
     if (bits == 4) body(std::integral_constant<int, 4>{});

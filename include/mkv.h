@@ -101,28 +101,31 @@ typedef struct mkv_tables {
  * rows (row index = "load index"):
  *
  *   INT-b (b = 4 or 2), F = 32/b codes per 32-bit word, LSB first:
- *     K codes   rows 0 .. b*2-1: lane slot L owns channels 8L..8L+7; for
+ *     K meta    4 rows: row 0 / 1 = scale of channels 8L+0..3 / 8L+4..7,
+ *               row 2 / 3 = min of the same channels (float32).  Key groups
+ *               run along tokens: one (scale, min) per channel for the 32
+ *               tokens of the block.
+ *     K codes   rows 0 .. 2b-1: lane slot L owns channels 8L..8L+7; for
  *               channel j = 8L + 4*(row & 1) + e (e = dword in the cell) the
  *               cell holds word w = row >> 1 of that channel.  Field i of word
- *               w of channel j (lane slot L) is the key code of token
- *               ((F*w + i) XOR f_S(L)) of the group, where
- *                 f_16(L) = 24*L3 ^ 14*L2 ^ 4*L1 ^ 2*L0  (d = 128)
- *                 f_8(L)  = 28*L2 ^ 8*L1 ^ 4*L0           (d = 64)
- *               and Lk is bit k of L.  Key quantization groups run along
- *               tokens: one (scale, min) per channel for the 32 tokens.
- *     K meta    4 rows: row 0 / 1 = scale of channels 8L+0..3 / 8L+4..7,
- *               row 2 / 3 = min of the same channels (float32).
- *     V codes   b*2 rows: lane slot L has value group G = L % NG and token
+ *               w of lane slot L is the key code of token tok(L, F*w + i):
+ *                 tok(L, r) = (r & 16) | ((r & 15) XOR f_S(L)),
+ *                 f_16(L) = 1*L0 ^ 2*L1 ^ 7*L2 ^ 12*L3   (d = 128)
+ *                 f_8(L)  = 2*L0 ^ 4*L1 ^ 14*L2           (d = 64)
+ *               where Lk is bit k of L.
+ *     V meta    4 rows: lane slot L has value group G = L % NG and token
  *               quarter tq = L / NG and covers tokens t_m = tq + 4m,
- *               m = 0..7, channels 32G..32G+31.  INT4: row m holds words
- *               u = 0..3 of token t_m, word u = channels 32G+8u .. +7.
- *               INT2: row m holds words of tokens t_{2m}, t_{2m+1} (two each,
- *               word u = channels 32G+16u .. +15).  Value groups run along
- *               channels: one (scale, min) per (token, 32 channels).
- *     V meta    4 rows: row m holds (scale, min) of token t_{2m} then
- *               (scale, min) of token t_{2m+1}, for group G (float32).
+ *               m = 0..7.  Row m holds (scale, min) of token t_{2m} then
+ *               (scale, min) of token t_{2m+1}, for group G (float32).  Value
+ *               groups run along channels: one (scale, min) per (token, 32
+ *               channels).
+ *     V codes   2b rows over channels 32G..32G+31 of the lane's tokens.
+ *               INT4: row m holds words u = 0..3 of token t_m, word u =
+ *               channels 32G+8u .. +7.  INT2: row m holds the two words of
+ *               token t_{2m} then those of t_{2m+1} (word u = channels
+ *               32G+16u .. +15).
  *   FP16 (bit-for-bit copies):
- *     K         32 rows: row r holds channels 8L..8L+7 of token r XOR f_S(L).
+ *     K         32 rows: row r holds channels 8L..8L+7 of token tok(L, r).
  *     V         32 rows: row r holds channels 32G + 8*(r & 3) .. +7 of token
  *               t_{r >> 2} (G, t_m as for INT-b values).
  *   Group block bytes: FP16 64*S*16, INT4 24*S*16, INT2 16*S*16.

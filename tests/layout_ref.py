@@ -15,16 +15,22 @@ GROUP = 32
 def tok_xor(S: int, L: int) -> int:
     b = [(L >> i) & 1 for i in range(4)]
     if S == 16:
-        return (24 * b[3]) ^ (14 * b[2]) ^ (4 * b[1]) ^ (2 * b[0])
+        return (1 * b[0]) ^ (2 * b[1]) ^ (7 * b[2]) ^ (12 * b[3])
     if S == 8:
-        return (28 * b[2]) ^ (8 * b[1]) ^ (4 * b[0])
+        return (2 * b[0]) ^ (4 * b[1]) ^ (14 * b[2])
     raise ValueError(S)
 
 
+def tok_of(S: int, L: int, r: int) -> int:
+    """Token held by key field position r (0..31) of lane slot L."""
+    return (r & 16) | ((r & 15) ^ tok_xor(S, L))
+
+
 def section_rows(bits: int):
+    """(key meta, key codes, value meta, value codes) rows of a group block."""
     if bits == 16:
-        return 32, 0, 32, 0
-    return 2 * bits, 4, 2 * bits, 4
+        return 0, 32, 0, 32
+    return 4, 2 * bits, 4, 2 * bits
 
 
 def group_bytes(bits: int, d: int) -> int:
@@ -39,7 +45,7 @@ def chunk_bytes(bits: int, d: int, C: int) -> int:
 def _maps(bits: int, d: int):
     """Index maps from (row, lane slot, dword, field) to (token, channel)."""
     S, NG = d // 8, d // 32
-    KC, KM, VC, VM = section_rows(bits)
+    KM, KC, VM, VC = section_rows(bits)
     m = {}
     if bits == 16:
         # K: row r, slot L, half-word e8 (0..7) -> token r^f(L), channel 8L+e8
@@ -51,7 +57,7 @@ def _maps(bits: int, d: int):
             for L in range(S):
                 G, tq = L % NG, L // NG
                 for e in range(8):
-                    kt[r, L, e] = r ^ tok_xor(S, L)
+                    kt[r, L, e] = tok_of(S, L, r)
                     kc[r, L, e] = 8 * L + e
                     vt[r, L, e] = tq + 4 * (r >> 2)
                     vc[r, L, e] = 32 * G + 8 * (r & 3) + e
@@ -64,7 +70,7 @@ def _maps(bits: int, d: int):
         for L in range(S):
             for e in range(4):
                 for i in range(F):
-                    kt[row, L, e, i] = (F * (row >> 1) + i) ^ tok_xor(S, L)
+                    kt[row, L, e, i] = tok_of(S, L, F * (row >> 1) + i)
                     kc[row, L, e, i] = 8 * L + 4 * (row & 1) + e
     vt = np.zeros((VC, S, 4, F), np.int64)
     vc = np.zeros((VC, S, 4, F), np.int64)
@@ -99,9 +105,9 @@ def decode_blocks(blocks: np.ndarray, bits: int, d: int) -> dict:
     INT-b: kq [N,32,d], ks [N,d], km [N,d], vq [N,32,d], vs [N,32,d/32], vm.
     FP16:  k [N,32,d], v [N,32,d] float16."""
     S, NG = d // 8, d // 32
-    KC, KM, VC, VM = section_rows(bits)
+    KM, KC, VM, VC = section_rows(bits)
     N = blocks.shape[0]
-    cells = np.ascontiguousarray(blocks).reshape(N, KC + KM + VC + VM, S, 16)
+    cells = np.ascontiguousarray(blocks).reshape(N, KM + KC + VM + VC, S, 16)
     m = _maps(bits, d)
     if bits == 16:
         kh = cells[:, :KC].copy().view(np.float16).reshape(N, KC, S, 8)
@@ -114,20 +120,18 @@ def decode_blocks(blocks: np.ndarray, bits: int, d: int) -> dict:
     F = 32 // bits
     mask = np.uint32((1 << bits) - 1)
     shifts = (np.arange(F, dtype=np.uint32) * np.uint32(bits))
-    kw = cells[:, :KC].copy().view(np.uint32).reshape(N, KC, S, 4)
+    kmeta = cells[:, 0:KM].copy().view(np.float32).reshape(N, 4, S, 4)
+    kw = cells[:, KM:KM + KC].copy().view(np.uint32).reshape(N, KC, S, 4)
+    vmeta = cells[:, KM + KC:KM + KC + VM].copy().view(np.float32).reshape(N, 4, S, 4)
+    vw = cells[:, KM + KC + VM:].copy().view(np.uint32).reshape(N, VC, S, 4)
     kfield = (kw[..., None] >> shifts) & mask
     kq = np.zeros((N, 32, d), np.uint8)
     kq[:, m["kt"], m["kc"]] = kfield.astype(np.uint8)
-    kmeta = cells[:, KC:KC + 4].copy().view(np.float32).reshape(N, 4, S, 4)
-    ks = np.concatenate([kmeta[:, 0], kmeta[:, 1]], axis=-1)          # [N, S, 8]
-    km = np.concatenate([kmeta[:, 2], kmeta[:, 3]], axis=-1)
-    ks = ks.reshape(N, d)
-    km = km.reshape(N, d)
-    vw = cells[:, KC + KM:KC + KM + VC].copy().view(np.uint32).reshape(N, VC, S, 4)
+    ks = np.concatenate([kmeta[:, 0], kmeta[:, 1]], axis=-1).reshape(N, d)      # [N, S, 8] -> [N, d]
+    km = np.concatenate([kmeta[:, 2], kmeta[:, 3]], axis=-1).reshape(N, d)
     vfield = (vw[..., None] >> shifts) & mask
     vq = np.zeros((N, 32, d), np.uint8)
     vq[:, m["vt"], m["vc"]] = vfield.astype(np.uint8)
-    vmeta = cells[:, KC + KM + VC:].copy().view(np.float32).reshape(N, 4, S, 4)
     vs = np.zeros((N, 32, NG), np.float32)
     vm = np.zeros((N, 32, NG), np.float32)
     is_scale = (np.arange(4) % 2 == 0)
