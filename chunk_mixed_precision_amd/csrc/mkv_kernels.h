@@ -8,8 +8,8 @@
 namespace mkv {
 
 // ---------------------------------------------------------------- router
-constexpr int kRouterBM = 128;   // tokens per workgroup tile
-constexpr int kRouterBI = 64;    // inner indices per workgroup tile (64 W1 + 64 W2 rows)
+constexpr int kRouterBM = 256;   // tokens per workgroup tile
+constexpr int kRouterBI = 128;   // inner indices per workgroup tile (128 W1 + 128 W2 rows)
 constexpr int kRouterBK = 32;    // K step staged in LDS
 
 struct RouterParams {

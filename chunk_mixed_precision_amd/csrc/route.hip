@@ -4,10 +4,10 @@
 //
 // Router: z = SiLU((x W1^T) .* (x W2^T)) W3^T + b3.  The two projections are
 // one bf16 GEMM on the MFMA units ([M x D] . [D x 2I], fp32 accumulation).
-// A workgroup owns 128 tokens x 64 inner indices: it computes both h1 and h2
+// A workgroup owns 256 tokens x 128 inner indices: it computes both h1 and h2
 // for those indices (W1 rows and the matching W2 rows share the tile), so the
 // gate and the W3 projection run in the epilogue and only 3 partial logits
-// per (token, 64-wide inner slice) reach memory.  The vote kernel sums the
+// per (token, 128-wide inner slice) reach memory.  The vote kernel sums the
 // slices in a fixed order, adds b3 and takes the argmax: results are
 // deterministic run to run.
 #include "mkv_internal.h"
@@ -19,134 +19,155 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glob_void;
 
-constexpr int BM = kRouterBM;          // 128 tokens
-constexpr int BI = kRouterBI;          // 64 inner indices -> 128 W12 rows
+constexpr int BM = kRouterBM;          // 256 tokens
+constexpr int BI = kRouterBI;          // 128 inner indices -> 256 W12 rows
 constexpr int BN = 2 * BI;
-constexpr int BK = kRouterBK;          // 32
-constexpr int LDK = BK + 8;            // padded LDS row (bf16 elements)
+constexpr int BK = kRouterBK;          // 32 bf16 = 64 B per row and stage
+constexpr int ROWB = BK * 2;           // bytes per tile row in LDS
+constexpr int STAGE = (BM + BN) * ROWB;   // A tile then B tile
+constexpr int LDA = BM / 2 + 1;        // epilogue: a[inner][128 tokens], padded row
+constexpr int LDS_BYTES = (2 * STAGE > BI * LDA * 4) ? 2 * STAGE : BI * LDA * 4;
+
+// 16-byte chunk c of tile row r sits at chunk c ^ ((r >> 1) & 3) of its
+// 64-byte LDS row: the eight rows read by one MFMA operand load then fall on
+// distinct bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3); }
 
 }  // namespace
 
-// 256 threads = 4 waves as 2 (tokens) x 2 (inner).  Wave (wm, wn) computes
-// tokens wm*64 .. +63 against W1 rows and W2 rows of inner indices
-// wn*32 .. +31 with 2 x 2 MFMA 32x32x16 blocks.
-__global__ __launch_bounds__(256) void router_gemm_kernel(RouterParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * LDK];
-    constexpr int STAGE = (BM + BN) * LDK;   // one stage: A tile then B tile
+// Router GEMM with the gate and the W3 projection fused in the epilogue.
+// Workgroup tile: 256 tokens x 128 inner indices (W1 and W2 rows of those
+// indices), K staged 32 at a time through two LDS buffers filled by
+// direct global->LDS loads.  256 threads = 4 waves as 2 (tokens) x 2 (inner);
+// wave (wm, wn) owns tokens wm*128..+127 and inner wn*64..+63: 4 x 4 MFMA
+// 32x32x16 bf16 blocks (two W1 and two W2 column blocks).  Tiles are ordered
+// so that the eight inner tiles of a token tile run on one XCD and share its
+// L2.
+__global__ __launch_bounds__(256, 1) void router_gemm_kernel(RouterParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const int m0 = blockIdx.x * BM;
-    const int i0 = blockIdx.y * BI;
+    const int NT = p.I / BI;
+    const int MT = (p.M + BM - 1) / BM;
+    // XCD-aware order: workgroup id -> (token tile, inner tile)
+    const int id = blockIdx.x;
+    const int xcd = id & 7, local = id >> 3;
+    const int mt = (local / NT) * 8 + xcd, nt = local % NT;
+    if (mt >= MT) return;
+    const int m0 = mt * BM, i0 = nt * BI;
     const int D = p.D;
 
-    // global -> LDS staging: each thread moves 2 x 16 B of A and 2 x 16 B of B per stage
-    int a_row[2], a_col[2], b_row[2];
-    const uint16_t* a_src[2];
-    const uint16_t* b_src[2];
-    bool a_ok[2];
+    // this lane's source rows for its 4 + 4 direct loads per stage: load j of
+    // wave w fills LDS bytes [(4w + j) KB, +1 KB) of the A (or B) region
+    const uint16_t* a_src[4];
+    const uint16_t* b_src[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int idx = tid + 256 * q;
-        a_row[q] = idx >> 2;
-        a_col[q] = (idx & 3) * 8;
-        a_ok[q] = (m0 + a_row[q]) < p.M;
-        a_src[q] = p.x + (size_t)(a_ok[q] ? m0 + a_row[q] : 0) * D + a_col[q];
-        b_row[q] = idx >> 2;
-        const int wrow = b_row[q] < BI ? i0 + b_row[q] : p.I + i0 + (b_row[q] - BI);
-        b_src[q] = p.w12 + (size_t)wrow * D + a_col[q];
+    for (int j = 0; j < 4; ++j) {
+        const int r = (wave * 4 + j) * 16 + (lane >> 2);     // tile row
+        const int c = swz(r, lane & 3);                      // logical chunk held by this slot
+        const int xr = min(m0 + r, p.M - 1);                 // rows past M read a valid row
+        a_src[j] = p.x + (size_t)xr * D + c * 8;
+        const int wr = r < BI ? i0 + r : p.I + i0 + (r - BI);
+        b_src[j] = p.w12 + (size_t)wr * D + c * 8;
     }
+    auto stage_load = [&](int buf, int k0) {
+        uint8_t* base = lds + buf * STAGE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_global_load_lds((glob_void*)(a_src[j] + k0),
+                                             (lds_void*)(base + (wave * 4 + j) * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glob_void*)(b_src[j] + k0),
+                                             (lds_void*)(base + BM * ROWB + (wave * 4 + j) * 1024), 16, 0, 0);
+        }
+    };
 
-    f32x16 acc[2][2];
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
 
-    uint4 ra[2], rb[2];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            ra[q] = a_ok[q] ? *reinterpret_cast<const uint4*>(a_src[q] + k0) : make_uint4(0, 0, 0, 0);
-            rb[q] = *reinterpret_cast<const uint4*>(b_src[q] + k0);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            *reinterpret_cast<uint4*>(lds + buf * STAGE + a_row[q] * LDK + a_col[q]) = ra[q];
-            *reinterpret_cast<uint4*>(lds + buf * STAGE + BM * LDK + b_row[q] * LDK + a_col[q]) = rb[q];
-        }
-    };
-
+    const int lr = lane & 31, lh = lane >> 5;
     const int nk = D / BK;
-    gload(0);
-    sstore(0);
+    stage_load(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int lr = lane & 31, lk = (lane >> 5) * 8;
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        const uint16_t* As = lds + cur * STAGE;
-        const uint16_t* Bs = As + BM * LDK;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+        if (kt + 1 < nk) stage_load(cur ^ 1, (kt + 1) * BK);
+        const uint8_t* As = lds + cur * STAGE;
+        const uint8_t* Bs = As + BM * ROWB;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 af[2], bfr[2];
+            const int c = 2 * ks + lh;
+            bf16x8 af[4], bfr[4];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                af[mb] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + mb * 32 + lr) * LDK + ks * 16 + lk);
+            for (int mb = 0; mb < 4; ++mb) {
+                const int r = wm * 128 + mb * 32 + lr;
+                af[mb] = *reinterpret_cast<const bf16x8*>(As + r * ROWB + swz(r, c) * 16);
+            }
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-                bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + (nb * BI + wn * 32 + lr) * LDK + ks * 16 + lk);
+            for (int nb = 0; nb < 4; ++nb) {
+                const int r = (nb < 2 ? 0 : BI) + wn * 64 + (nb & 1) * 32 + lr;
+                bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + r * ROWB + swz(r, c) * 16);
+            }
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < 4; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
         }
-        if (kt + 1 < nk) {
-            sstore(cur ^ 1);
-        }
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    // ---------------- epilogue: gate, then this slice's share of W3
-    float* a_lds = reinterpret_cast<float*>(lds);     // [BM][BI + 1]
-    constexpr int LDA = BI + 1;
+    // ---------------- epilogue: a = SiLU(h1 * h2), then this tile's share of
+    // z = a W3^T, in two rounds of 128 tokens through LDS as a[inner][token]
+    float* a_lds = reinterpret_cast<float*>(lds);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int round = 0; round < 2; ++round) {
+        if (wm == round) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int tok = wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int ii = wn * 32 + lr;
-            const float u = acc[mb][0][r] * acc[mb][1][r];
-            const float a = u / (1.0f + expf(-u));
-            a_lds[tok * LDA + ii] = a;
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int tok = mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const int ii = wn * 64 + nb * 32 + lr;
+                        const float u = acc[mb][nb][r] * acc[mb][nb + 2][r];
+                        a_lds[ii * LDA + tok] = u / (1.0f + expf(-u));
+                    }
         }
-    __syncthreads();
-    {
-        const int tok = tid >> 1, half = tid & 1;
-        const float* arow = a_lds + tok * LDA + half * 32;
-        const float* w3 = p.w3 + i0 + half * 32;
-        float z0 = 0.f, z1 = 0.f, z2 = 0.f;
-        for (int i = 0; i < 32; ++i) {
-            const float a = arow[i];
-            z0 = __builtin_fmaf(a, w3[i], z0);
-            z1 = __builtin_fmaf(a, w3[p.I + i], z1);
-            z2 = __builtin_fmaf(a, w3[2 * p.I + i], z2);
+        __syncthreads();
+        {
+            const int tok = tid >> 1, half = tid & 1;
+            const float* w3 = p.w3 + i0 + half * 64;
+            float z0 = 0.f, z1 = 0.f, z2 = 0.f;
+            for (int i = 0; i < 64; ++i) {
+                const float a = a_lds[(half * 64 + i) * LDA + tok];
+                z0 = __builtin_fmaf(a, w3[i], z0);
+                z1 = __builtin_fmaf(a, w3[p.I + i], z1);
+                z2 = __builtin_fmaf(a, w3[2 * p.I + i], z2);
+            }
+            // fixed order: lower half + upper half
+            const float y0 = __shfl_xor(z0, 1), y1 = __shfl_xor(z1, 1), y2 = __shfl_xor(z2, 1);
+            const int row = m0 + round * 128 + tok;
+            if (half == 0 && row < p.M) {
+                float* zp = p.zpart + ((size_t)nt * p.M + row) * 3;
+                zp[0] = z0 + y0;
+                zp[1] = z1 + y1;
+                zp[2] = z2 + y2;
+            }
         }
-        // fixed order: lower half + upper half on both lanes of the pair
-        const float y0 = __shfl_xor(z0, 1), y1 = __shfl_xor(z1, 1), y2 = __shfl_xor(z2, 1);
-        if (half == 0 && m0 + tok < p.M) {
-            float* zp = p.zpart + ((size_t)blockIdx.y * p.M + m0 + tok) * 3;
-            zp[0] = z0 + y0;
-            zp[1] = z1 + y1;
-            zp[2] = z2 + y2;
-        }
+        __syncthreads();
     }
 }
 
@@ -239,8 +260,9 @@ __global__ __launch_bounds__(256) void reorder_kernel(ReorderParams p) {
 }
 
 hipError_t launch_router(const RouterParams& rp, hipStream_t st) {
-    const dim3 grid((rp.M + BM - 1) / BM, rp.I / BI);
-    router_gemm_kernel<<<grid, 256, 0, st>>>(rp);
+    const int MT = (rp.M + BM - 1) / BM;
+    const int MT8 = (MT + 7) / 8 * 8;
+    router_gemm_kernel<<<dim3(MT8 * (rp.I / BI)), 256, 0, st>>>(rp);
     return hipGetLastError();
 }
 

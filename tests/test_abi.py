@@ -52,7 +52,7 @@ def test_group_bytes(bits, d, expect):
 
 def test_pool_and_workspace_bytes():
     assert mkv.pool_bytes(4, 2, 3, 5, 128, 256) == 2 * 3 * 5 * 8 * 6144
-    assert mkv.workspace_bytes_route(2, 1024, 256, 128) == (128 // 64) * 2 * 1024 * 3 * 4
+    assert mkv.workspace_bytes_route(2, 1024, 256, 256) == (256 // 128) * 2 * 1024 * 3 * 4
     w = mkv.workspace_bytes_attention(1, 32, 32, 128, 256, [4, 115, 9])
     assert w > 0
     assert mkv.workspace_bytes_attention(1, 3, 2, 128, 256, [1, 1, 1]) == 0
@@ -91,6 +91,7 @@ def test_route_argument_errors():
     assert route(T=200) == E.MKV_ERR_UNSUPPORTED
     assert route(D=100) == E.MKV_ERR_UNSUPPORTED
     assert route(I=100) == E.MKV_ERR_UNSUPPORTED
+    assert route(I=192) == E.MKV_ERR_UNSUPPORTED
     assert route(x=0x101) == E.MKV_ERR_ARG                       # misaligned
     assert route(off=1) == E.MKV_ERR_ARG                         # offset without MKV_APPEND
     assert route(tab=_tables(n_max=1)) == E.MKV_ERR_ARG          # 2 chunks > n_max
