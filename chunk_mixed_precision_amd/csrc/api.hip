@@ -20,23 +20,23 @@ inline int hip_status(hipError_t e) {
     return MKV_ERR_HIP;
 }
 
-// Attention work split.  The bytes of each (sequence, KV head) are cut into
-// parts of about per_wave bytes, one 64-lane wavefront per part; per_wave is
-// chosen so that the whole cache (at capacity) needs about kAttnWaves
-// wavefronts, i.e. one resident round on 256 CUs (12 per CU at the kernel's
-// register use), with a floor that keeps every wavefront busy for a while.
-constexpr long long kAttnWaves = 3072;
-constexpr long long kMinWaveBytes = 16384;
+// Attention work split: persistent workgroups of mkv::kAttnWaves wavefronts,
+// one per CU (256 on MI355X), each taking an equal byte range of the cache;
+// fewer when the cache at capacity is small (every range at least
+// mkv::kAttnMinWgBytes).  The device recomputes the split from the actual
+// segment counts and may use fewer still.  Partials: one record per
+// (sequence, head) plus one per workgroup boundary.
+constexpr long long kAttnWorkgroups = 256;
 
-inline void attn_split(int B, int Hkv, int d, const int* cap, int C, long long& per_wave, int& nt_total) {
+inline int attn_workgroups(int B, int Hkv, int d, const int* cap, int C) {
     const int bits[3] = {16, 4, 2};
     long long bh_bytes = 0;
     for (int k = 0; k < 3; ++k) bh_bytes += (long long)cap[k] * (C / mkv::kGroup) * (long long)mkv::group_bytes(bits[k], d);
     const long long total = bh_bytes * B * Hkv;
-    per_wave = (total + kAttnWaves - 1) / kAttnWaves;
-    if (per_wave < kMinWaveBytes) per_wave = kMinWaveBytes;
-    const long long nw_max = (bh_bytes + per_wave - 1) / per_wave;
-    nt_total = (int)(3 * (nw_max > 0 ? nw_max : 1));
+    long long g = total / mkv::kAttnMinWgBytes;
+    if (g > kAttnWorkgroups) g = kAttnWorkgroups;
+    if (g < 1) g = 1;
+    return (int)g;
 }
 
 inline bool valid_cache(const mkv_cache* c) {
@@ -96,10 +96,8 @@ size_t mkv_workspace_bytes(int op, int a, int b, int c, int e, int f, const int*
     if (op == MKV_OP_ATTENTION) {
         const int B = a, Hq = b, Hkv = c, d = e, C = f;
         if (!caps || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (d != 64 && d != 128) || C <= 0 || C % 32) return 0;
-        long long pw;
-        int ntt;
-        attn_split(B, Hkv, d, caps, C, pw, ntt);
-        return (size_t)B * Hkv * ntt * (Hq / Hkv) * (d + 4) * sizeof(float) + 16;
+        const int G = attn_workgroups(B, Hkv, d, caps, C);
+        return ((size_t)B * Hkv + G) * (Hq / Hkv) * (d + 4) * sizeof(float) + 16;
     }
     return 0;
 }
@@ -203,7 +201,7 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq, const mkv_cache* c
     }
     ap.seg_count = cache->seg_count;
     ap.B = cache->B; ap.Hkv = cache->Hkv; ap.Hq = Hq; ap.C = cache->C;
-    attn_split(cache->B, cache->Hkv, cache->d, cache->cap, cache->C, ap.per_wave, ap.nt_total);
+    ap.G = attn_workgroups(cache->B, cache->Hkv, cache->d, cache->cap, cache->C);
     ap.part = static_cast<float*>(workspace);
     ap.tail_k = static_cast<const uint16_t*>(tail_k_fp16);
     ap.tail_v = static_cast<const uint16_t*>(tail_v_fp16);

@@ -1,17 +1,27 @@
 // Split-K decode attention over the mixed-bitwidth packed cache
 // (MoQAE "Overall framework": ordinary attention after quantization;
 // Cocktail abstract: chunk-level computation over bitwidth-contiguous
-// segments, so every tile below has a single bitwidth and no wavefront ever
-// branches on bitwidth inside its inner loop).
+// segments, so every work unit below has a single bitwidth and no wavefront
+// ever branches on bitwidth inside its inner loop).
 //
-// Work: the packed bytes of each (sequence, KV head) (its FP16, INT4 and INT2
-// segments in that order) are cut into equal-byte parts, one 64-lane
-// wavefront per part; a part crossing a segment boundary is processed as one
-// single-bitwidth piece per segment, each leaving one partial.  A wave is
-// split into R = 64/S rows of S = d/8 lanes; each row handles one group
-// block per iteration (GQA: the rows of one iteration take the same group
-// for different query heads).  Inside a row, lane slot L owns channels
-// 8L..8L+7 of the keys and value group L % (d/32) of tokens L / (d/32) + 4m.
+// Work.  The packed bytes of each (sequence, KV head) -- its FP16, INT4 and
+// INT2 segments in that order -- are cut into units of one wavefront
+// iteration (GPI group blocks of one segment).  All (sequence, head) streams
+// are laid end to end and split into equal byte ranges, one per workgroup of
+// kAttnWaves wavefronts (one CU's worth); a range may span several
+// (sequence, head) streams, each giving one "piece".  Inside a piece the
+// wavefronts take units from a workgroup-local ticket counter in LDS, so a
+// wavefront that the CU's scheduler favours simply takes more units and all
+// of them finish together.  Each wavefront keeps one online-softmax state
+// across the units (and bitwidths) it takes; at the end of a piece the
+// workgroup merges its wavefronts' states in LDS and writes one partial.  A
+// second launch merges the partials of each (sequence, head).
+//
+// A wavefront is split into R = 64/S rows of S = d/8 lanes; each row handles
+// one group block per iteration (GQA: the rows of one iteration take the
+// same group for different query heads).  Inside a row, lane slot L owns
+// channels 8L..8L+7 of the keys and value group L % (d/32) of tokens
+// L / (d/32) + 4m.
 //
 // Scores: s_t = sum_j q_j * (code_tj * s_j + mn_j) is evaluated as
 // sum_j (q_j s_j) code_tj + sum_j q_j mn_j, so key dequantization costs one
@@ -78,12 +88,15 @@ __device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_c
 // FP16: 8 phases: key rows 0-31, then value rows 0-31.
 template <int BITS> __host__ __device__ constexpr int n_phases() { return BITS == 16 ? 8 : (BITS == 4 ? 3 : 2); }
 
+// Rows 8*phase .. 8*phase+7 of the group block at base + voff (base is
+// wave-uniform, voff = this lane's byte offset: its row's block and its
+// 16-byte cell).
 template <int D>
-__device__ __forceinline__ void load_rows8(uint4* buf, const uint8_t* gp, int phase, int L) {
+__device__ __forceinline__ void load_rows8(uint4* buf, const uint8_t* base, uint32_t voff, int phase) {
     constexpr size_t ROWB = (size_t)(D / 8) * 16;
-    const uint8_t* src = gp + (size_t)phase * 8 * ROWB + L * 16;
+    const uint8_t* src = base + (size_t)phase * 8 * ROWB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) buf[i] = ld16(src + i * ROWB);
+    for (int i = 0; i < 8; ++i) buf[i] = ld16(src + voff + i * ROWB);
 }
 
 // Reduce-scatter of one half (16 per-token partial sums) over the S lanes of
@@ -121,39 +134,193 @@ __device__ __forceinline__ void merge_run(float& m, float& l, float* o, float m2
     m = mn;
 }
 
-template <int BITS, int D, int HB>
-__device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, int slot, int g0, int g1) {
+
+// ---------------------------------------------------------------- work map
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ long long uniform64(long long x) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long long)x);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// Units of one (sequence, head) stream.  Every head of a sequence has the
+// same segment sizes, so the geometry depends on the sequence only.
+template <int D, int HB>
+struct SeqUnits {
+    static constexpr int GPI = (512 / D) / HB;      // group blocks per unit
+    int segg[3];        // group blocks written in each segment
+    int nu[3];          // units in each segment
+    int ubase[3];       // index of each segment's first unit
+    long long soff[3];  // byte offset of each segment's first unit in the stream
+    long long bytes;    // bytes of the whole stream (units x unit bytes)
+    int units;
+
+    static constexpr long long unit_bytes(int k) { return (long long)GPI * (long long)group_bytes(bits_of_expert(k), D); }
+
+    __device__ __forceinline__ void init(const AttnParams& p, int b) {
+        const int gpc = p.C / kGroup;
+        long long off = 0;
+        int u = 0;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            // chunks beyond a pool's capacity were never written: never read them
+            const int cnt = min(max(p.seg_count[b * 3 + k], 0), p.cap[k]);
+            segg[k] = cnt * gpc;
+            nu[k] = (segg[k] + GPI - 1) / GPI;
+            ubase[k] = u;
+            soff[k] = off;
+            u += nu[k];
+            off += (long long)nu[k] * unit_bytes(k);
+        }
+        units = u;
+        bytes = off;
+    }
+
+    // Index of the first unit whose first byte is at or after stream offset x
+    // (units when there is none).
+    __device__ __forceinline__ int first_at_or_after(long long x) const {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            if (nu[k] == 0) continue;
+            const long long rel = x - soff[k];
+            const long long u = rel <= 0 ? 0 : (rel + unit_bytes(k) - 1) / unit_bytes(k);
+            if (u < nu[k]) return ubase[k] + (int)u;
+        }
+        return units;
+    }
+
+    __device__ __forceinline__ long long unit_start(int U) const {
+        if (U < ubase[1]) return soff[0] + (long long)(U - ubase[0]) * unit_bytes(0);
+        if (U < ubase[2]) return soff[1] + (long long)(U - ubase[1]) * unit_bytes(1);
+        return soff[2] + (long long)(U - ubase[2]) * unit_bytes(2);
+    }
+};
+
+// Bytes of the whole cache (every (sequence, head) stream), computed by one
+// wavefront with one sequence per lane; every lane gets the result.
+template <int D, int HB>
+__device__ __forceinline__ long long total_bytes(const AttnParams& p) {
+    const int lane = threadIdx.x & 63;
+    long long t = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+        const int b = b0 + lane;
+        long long x = 0;
+        if (b < p.B) {
+            SeqUnits<D, HB> su;
+            su.init(p, b);
+            x = su.bytes;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+        t += x;
+    }
+    return uniform64(t * p.Hkv);
+}
+
+// Workgroups actually used: at most G, and few enough that every range is at
+// least kAttnMinWgBytes long (longer than any unit, so each workgroup
+// between the first and the last owner of a stream owns a unit of it).
+__device__ __forceinline__ int used_workgroups(const AttnParams& p, long long total) {
+    const long long g = total / kAttnMinWgBytes;
+    return (int)max(1LL, min((long long)p.G, g));
+}
+
+// The workgroup whose byte range contains global offset x:
+// range w = [floor(w*T/G), floor((w+1)*T/G)).
+__device__ __forceinline__ int owner_of(long long x, long long total, int G) {
+    return (int)(((x + 1) * (long long)G - 1) / total);
+}
+
+// Global offset of sequence b's first stream (head 0): Hkv * sum of the
+// stream bytes of sequences 0 .. b-1.  One wavefront, every lane gets it.
+template <int D, int HB>
+__device__ __forceinline__ long long seq_offset(const AttnParams& p, int b) {
+    const int lane = threadIdx.x & 63;
+    long long t = 0;
+    for (int b0 = 0; b0 < b; b0 += 64) {
+        const int bb = b0 + lane;
+        long long x = 0;
+        if (bb < b) {
+            SeqUnits<D, HB> su;
+            su.init(p, bb);
+            x = su.bytes;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+        t += x;
+    }
+    return uniform64(t * p.Hkv);
+}
+
+// The sequence whose streams contain global offset x (x < total), and the
+// global offset of its first stream.  One wavefront, uniform result.
+template <int D, int HB>
+__device__ __forceinline__ int seq_containing(const AttnParams& p, long long x, long long& seq_off) {
+    const int lane = threadIdx.x & 63;
+    long long carry = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+        const int b = b0 + lane;
+        long long v = 0;
+        if (b < p.B) {
+            SeqUnits<D, HB> su;
+            su.init(p, b);
+            v = su.bytes * p.Hkv;
+        }
+        // inclusive prefix over the lanes
+        long long incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        const unsigned long long hit = __ballot(b < p.B && carry + incl > x);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            seq_off = uniform64(carry + __shfl(incl - v, l));
+            return b0 + l;
+        }
+        carry = uniform64(carry + __shfl(incl, 63));
+    }
+    seq_off = carry;
+    return p.B;
+}
+
+// ---------------------------------------------------------------- one piece
+// Units [U0, U1) of the stream of (b, h), processed by the kAttnWaves
+// wavefronts of the workgroup, which take units from the ticket counter
+// *ctr.  Leaves one partial per query head of the group at record `slot`.
+template <int D, int HB>
+__device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D, HB>& su, int b, int h, int U0,
+                                          int U1, int slot, int* ctr, float (*plds)[32], float* rec) {
     constexpr int S = D / 8;
     constexpr int R = 64 / S;          // rows per wave
     constexpr int NG = D / 32;         // value groups per token
-    constexpr int GPI = R / HB;        // group blocks per iteration
+    constexpr int GPI = R / HB;        // group blocks per unit
     constexpr int NTH = 16 / S;        // tokens per lane and key half after the reduce-scatter
-    constexpr int NPH = n_phases<BITS>();
-    constexpr size_t GB = group_bytes(BITS, D);
+    constexpr int RECF = D + 4;        // floats per merged record
 
-    __shared__ float plds[R][32];
-
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = lane / S, L = lane % S;
     const int hb = row % HB, gslot = row / HB;
     const int G = L % NG, tq = L / NG;
     const int fx = tok_xor(S, L);
-    const int C = p.C;
-    const int b = bh / p.Hkv, h = bh % p.Hkv;
+    const int bh = b * p.Hkv + h;
     const int hq = h * HB + hb;
 
-    const uint8_t* seg = p.pool[k] + (size_t)bh * p.cap[k] * (C / kGroup) * GB;
+    if (threadIdx.x == 0) *ctr = U0;
+    __syncthreads();
+
+    // segment base pointers of this (b, h)
+    const size_t gpc = (size_t)(p.C / kGroup);
+    const uint8_t* seg16 = p.pool[0] + (size_t)bh * p.cap[0] * gpc * group_bytes(16, D);
+    const uint8_t* seg4 = p.pool[1] + (size_t)bh * p.cap[1] * gpc * group_bytes(4, D);
+    const uint8_t* seg2 = p.pool[2] + (size_t)bh * p.cap[2] * gpc * group_bytes(2, D);
 
     // query channels 8L..8L+7 of head hq
     const uint4 qc = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + hq) * D + 8 * L);
     const uint32_t qw[4] = {qc.x, qc.y, qc.z, qc.w};
-    float qs[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        qs[2 * e] = lo_h(qw[e]) * p.qscale;
-        qs[2 * e + 1] = hi_h(qw[e]) * p.qscale;
-    }
     const half2_t qh0 = as_h2(qw[0]), qh1 = as_h2(qw[1]), qh2 = as_h2(qw[2]), qh3 = as_h2(qw[3]);
+    float qs[8];           // q * log2(e)/sqrt(d) in fp32 (INT-b keys), set after the FP16 segment
 
     float M = -INFINITY;   // running max of this row (log2 domain), row-uniform
     float lsum = 0.f;      // this lane's share of the softmax denominator
@@ -167,11 +334,6 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
     float qp[8];           // q_j * s_j (INT-b), this group
     float bias = 0.f;      // sum_j q_j * mn_j over this lane's channels (INT-b)
     float acc[16];
-
-    auto group_ptr = [&](int gbase) {
-        const int gi = gbase + gslot;
-        return seg + (size_t)(gi < g1 ? gi : g1 - 1) * GB;
-    };
 
     // ---- online-softmax update from sc[], probabilities to the value layout
     auto softmax_step = [&](bool valid) {
@@ -212,7 +374,6 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         pw[0] = pa.x; pw[1] = pa.y; pw[2] = pa.z; pw[3] = pa.w;
         pw[4] = pb.x; pw[5] = pb.y; pw[6] = pb.z; pw[7] = pb.w;
     };
-
     // ---- INT-b pieces
     auto key_meta = [&](const uint4* m4) {           // rows: scale lo, scale hi, min lo, min hi
         const float4 s0 = as_f4(m4[0]), s1 = as_f4(m4[1]), n0 = as_f4(m4[2]), n1 = as_f4(m4[3]);
@@ -349,8 +510,10 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         }
     };
 
+
     // one phase's arithmetic on the rows in `cur`
-    auto compute_phase = [&](int ph, const uint4* cur, bool valid) {
+    auto compute_phase = [&](auto bits_tag, int ph, const uint4* cur, bool valid) {
+        constexpr int BITS = decltype(bits_tag)::value;
         if constexpr (BITS == 4) {
             if (ph == 0) {
                 key_meta(cur);
@@ -393,52 +556,108 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         }
     };
 
-    // ---- main loop.  Every phase's loads are issued one phase ahead, into
-    // the other of two 8-row register buffers; the last phase of a group
-    // prefetches the next group's first phase (or, at the end, re-reads this
-    // group: a cache hit that keeps the loop free of a branch whose merge
-    // point would make the compiler wait for every outstanding load).
+    // ---- unit loop.  Every phase's loads are issued one phase ahead, into
+    // the other of two 8-row register buffers; the last phase of a unit
+    // prefetches the first phase of the next unit this wavefront holds a
+    // ticket for (or, when there is none, re-reads its own: a cache hit that
+    // keeps the loop free of a branch whose merge point would make the
+    // compiler wait for every outstanding load).  Tickets are taken in
+    // increasing order, so a wavefront meets the segments in the order FP16,
+    // INT4, INT2 and the three loops below run once each.
     uint4 bufA[8], bufB[8];
-    auto run_group = [&](auto par_tag, int gbase, const uint8_t* gp, const uint8_t* gn) {
+    auto grab = [&]() -> int {
+        int t = 0;
+        if (lane == 0) t = atomicAdd(ctr, 1);
+        return __builtin_amdgcn_readfirstlane(t);
+    };
+    // Unit U (any segment): the wave-uniform address of its first group
+    // block and this lane's offset from there (its row's block, rows past the
+    // end of the segment re-read the first block, and its 16-byte cell).
+    auto unit_addr = [&](int U, uint32_t& voff) -> const uint8_t* {
+        int k = 0, u = U;
+        const uint8_t* base = seg16;
+        uint32_t gb = (uint32_t)group_bytes(16, D);
+        if (U >= su.ubase[2]) {
+            k = 2; u = U - su.ubase[2]; base = seg2; gb = (uint32_t)group_bytes(2, D);
+        } else if (U >= su.ubase[1]) {
+            k = 1; u = U - su.ubase[1]; base = seg4; gb = (uint32_t)group_bytes(4, D);
+        }
+        const int segg = k == 0 ? su.segg[0] : (k == 1 ? su.segg[1] : su.segg[2]);
+        const bool live = u * GPI + gslot < segg;
+        voff = (live ? (uint32_t)gslot * gb : 0u) + (uint32_t)L * 16u;
+        return base + (size_t)u * GPI * gb;
+    };
+    auto run_unit = [&](auto bits_tag, auto par_tag, const uint8_t* ub, uint32_t vo, const uint8_t* ubn,
+                        uint32_t von, bool valid) {
+        constexpr int BITS = decltype(bits_tag)::value;
         constexpr int PAR = decltype(par_tag)::value;
-        const bool valid = gbase + gslot < g1;
+        constexpr int NPH = n_phases<BITS>();
 #pragma unroll
         for (int ph = 0; ph < NPH; ++ph) {
             uint4* cur = ((ph + PAR) & 1) ? bufB : bufA;
             uint4* nxt = ((ph + PAR) & 1) ? bufA : bufB;
-            load_rows8<D>(nxt, ph + 1 < NPH ? gp : gn, ph + 1 < NPH ? ph + 1 : 0, L);
+            if (ph + 1 < NPH) load_rows8<D>(nxt, ub, vo, ph + 1);
+            else load_rows8<D>(nxt, ubn, von, 0);
             __builtin_amdgcn_sched_barrier(0);
-            compute_phase(ph, cur, valid);
+            compute_phase(bits_tag, ph, cur, valid);
         }
     };
-    const uint8_t* gp = group_ptr(g0);
-    load_rows8<D>(bufA, gp, 0, L);
-    if constexpr (NPH % 2 == 0) {
-        for (int gbase = g0; gbase < g1; gbase += GPI) {
-            const uint8_t* gn = gbase + GPI < g1 ? group_ptr(gbase + GPI) : gp;
-            run_group(std::integral_constant<int, 0>{}, gbase, gp, gn);
-            gp = gn;
+
+    int U = grab();
+    uint32_t vo = 0;
+    const uint8_t* ub = seg16;
+    if (U < U1) {
+        ub = unit_addr(U, vo);
+        load_rows8<D>(bufA, ub, vo, 0);
+    }
+    // one step: process unit U (whose first phase is in the buffer of parity
+    // PAR) and move to the next ticket; with no next unit the prefetch
+    // re-reads this one
+    auto step = [&](auto bits_tag, auto par_tag, int k, int segg_k, int ubase_k) {
+        const int Un = grab();
+        uint32_t von = vo;
+        const uint8_t* ubn = ub;
+        if (Un < U1) ubn = unit_addr(Un, von);
+        const bool valid = (U - ubase_k) * GPI + gslot < segg_k;
+        run_unit(bits_tag, par_tag, ub, vo, ubn, von, valid);
+        U = Un;
+        ub = ubn;
+        vo = von;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    {   // FP16 (even phase count: buffer parity is kept)
+        const int end = min(U1, su.ubase[0] + su.nu[0]);
+        while (U < end) step(std::integral_constant<int, 16>{}, I0{}, 0, su.segg[0], su.ubase[0]);
+    }
+    // the FP16 keys used the raw fp16 query; the INT-b keys take fp32 weights
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        qs[2 * e] = lo_h(qw[e]) * p.qscale;
+        qs[2 * e + 1] = hi_h(qw[e]) * p.qscale;
+    }
+    {   // INT4 (odd phase count: parity flips every unit, so units go in pairs)
+        const int end = min(U1, su.ubase[1] + su.nu[1]);
+        bool flipped = false;
+        while (U < end) {
+            step(std::integral_constant<int, 4>{}, I0{}, 1, su.segg[1], su.ubase[1]);
+            if (U >= end) { flipped = true; break; }
+            step(std::integral_constant<int, 4>{}, I1{}, 1, su.segg[1], su.ubase[1]);
         }
-    } else {
-        // odd phase count: buffer parity flips every group, so groups go in pairs
-        for (int gbase = g0; gbase < g1; gbase += 2 * GPI) {
-            const uint8_t* gn = gbase + GPI < g1 ? group_ptr(gbase + GPI) : gp;
-            run_group(std::integral_constant<int, 0>{}, gbase, gp, gn);
-            if (gbase + GPI < g1) {
-                const uint8_t* gn2 = gbase + 2 * GPI < g1 ? group_ptr(gbase + 2 * GPI) : gn;
-                run_group(std::integral_constant<int, 1>{}, gbase + GPI, gn, gn2);
-                gp = gn2;
-            } else {
-                gp = gn;
-            }
+        if (flipped) {
+            // the next unit's first phase landed in bufB
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bufA[i] = bufB[i];
         }
+    }
+    {   // INT2 (even phase count)
+        const int end = min(U1, su.ubase[2] + su.nu[2]);
+        while (U < end) step(std::integral_constant<int, 2>{}, I0{}, 2, su.segg[2], su.ubase[2]);
     }
 
     // ---------------- merge rows of the same head, then lanes of the same value group
-    if constexpr (BITS != 16) {
 #pragma unroll
-        for (int c = 0; c < 32; ++c) o[c] += pm;
-    }
+    for (int c = 0; c < 32; ++c) o[c] += pm;
     float Mx = M;
 #pragma unroll
     for (int off = S * HB; off < 64; off <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, off));
@@ -459,107 +678,118 @@ __device__ __forceinline__ void tile_body(const AttnParams& p, int k, int bh, in
         for (int off = S * HB; off < 64; off <<= 1) v += __shfl_xor(v, off);
         o[c] = v;
     }
+    // ---------------- merge the wavefronts of the workgroup in LDS
     if (row == hb && tq == 0) {
-        float* rec = p.part + (((size_t)bh * p.nt_total + slot) * HB + hb) * (D + 4);
-        float4* o4 = reinterpret_cast<float4*>(rec + 32 * G);
+        float* r = rec + ((size_t)wave * HB + hb) * RECF;
+        float4* o4 = reinterpret_cast<float4*>(r + 32 * G);
 #pragma unroll
         for (int c = 0; c < 8; ++c) o4[c] = make_float4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
-        if (G == 0) *reinterpret_cast<float4*>(rec + D) = make_float4(Mx, lsum, 0.f, 0.f);
+        if (G == 0) {
+            r[D] = Mx;
+            r[D + 1] = lsum;
+        }
     }
-
-}
-
-// Equal-byte split of one (sequence, KV head).  Its three segments, taken
-// in the order FP16, INT4, INT2, form one byte range of `total` bytes that
-// is cut into nw = ceil(total / per_wave) near-equal parts; part w covers
-// bytes [w*total/nw, (w+1)*total/nw).  A group block belongs to the part
-// that contains its first byte.  Every wavefront (and the combine) derives
-// the same split from seg_count, so no schedule is stored.
-struct Split {
-    int segg[3];        // group blocks in each segment
-    long long pre[3];   // first byte of each segment
-    long long total;
-    int nw;
-};
-
-template <int D>
-__device__ __forceinline__ Split split_of(const AttnParams& p, int b) {
-    Split sp;
-    const int gpc = p.C / kGroup;
-    sp.total = 0;
+    __syncthreads();
+    constexpr int QPR = D / 4;
+    if ((int)threadIdx.x < HB * QPR) {
+        const int mh = threadIdx.x / QPR, qd = threadIdx.x % QPR;
+        float m = -INFINITY, l = 0.f, oo[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        // chunks beyond a pool's capacity were never written: never read them
-        sp.segg[k] = min(p.seg_count[b * 3 + k], p.cap[k]) * gpc;
-        sp.pre[k] = sp.total;
-        sp.total += (long long)sp.segg[k] * (long long)group_bytes(bits_of_expert(k), D);
+        for (int wv = 0; wv < kAttnWaves; ++wv) {
+            const float* r = rec + ((size_t)wv * HB + mh) * RECF;
+            const float4 x = *reinterpret_cast<const float4*>(r + 4 * qd);
+            const float o2[4] = {x.x, x.y, x.z, x.w};
+            merge_run<4>(m, l, oo, r[D], r[D + 1], o2);
+        }
+        float* dst = p.part + ((size_t)slot * HB + mh) * RECF;
+        *reinterpret_cast<float4*>(dst + 4 * qd) = make_float4(oo[0], oo[1], oo[2], oo[3]);
+        if (qd == 0) *reinterpret_cast<float4*>(dst + D) = make_float4(m, l, 0.f, 0.f);
     }
-    sp.nw = (int)((sp.total + p.per_wave - 1) / p.per_wave);
-    return sp;
-}
-
-// Group range [g0, g1) of segment k owned by part w.
-template <int D>
-__device__ __forceinline__ void part_groups(const Split& sp, int w, int k, int& g0, int& g1) {
-    const long long gb = (long long)group_bytes(bits_of_expert(k), D);
-    const long long o0 = (long long)w * sp.total / sp.nw - sp.pre[k];
-    const long long o1 = (long long)(w + 1) * sp.total / sp.nw - sp.pre[k];
-    long long a = o0 <= 0 ? 0 : (o0 + gb - 1) / gb;
-    long long c = o1 <= 0 ? 0 : (o1 + gb - 1) / gb;
-    g0 = (int)(a < sp.segg[k] ? a : sp.segg[k]);
-    g1 = (int)(c < sp.segg[k] ? c : sp.segg[k]);
+    __syncthreads();
 }
 
 }  // namespace
 
-// grid (nw_max, B*Hkv): wavefront (w, bh) streams part w of (b, h), one
-// single-bitwidth piece per segment it overlaps, and writes one partial per
-// piece at slot (w, k).
+// Persistent workgroups of kAttnWaves wavefronts.  Workgroup w takes the byte
+// range [w*T/G, (w+1)*T/G) of the end-to-end (sequence, head) streams (T
+// bytes in all) and, for every stream whose unit starts fall in it, runs
+// those units as one piece and leaves the piece's partial at record
+// (sequence*Hkv + head) + w.
 template <int D, int HB>
-__global__ __launch_bounds__(64, 3) void attn_tile_kernel(AttnParams p) {
-    const int w = blockIdx.x, bh = blockIdx.y;
-    const int b = bh / p.Hkv;
-    const Split sp = split_of<D>(p, b);
-    if (w >= sp.nw) return;
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        int g0, g1;
-        part_groups<D>(sp, w, k, g0, g1);
-        const int slot = w * 3 + k;
-        if (g0 >= g1) {
-            // empty piece: mark it so the combine skips it
-            if (threadIdx.x < HB) {
-                float* rec = p.part + (((size_t)bh * p.nt_total + slot) * HB + threadIdx.x) * (D + 4);
-                *reinterpret_cast<float4*>(rec + D) = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-            }
-            continue;
+__global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_kernel(AttnParams p) {
+    __shared__ int ctr;
+    __shared__ float plds_all[kAttnWaves][64 / (D / 8)][32];
+    __shared__ __align__(16) float rec[kAttnWaves * HB * (D + 4)];
+    const int w = blockIdx.x;
+    const long long total = total_bytes<D, HB>(p);
+    if (total == 0) return;
+    const int G = used_workgroups(p, total);
+    if (w >= G) return;
+    const long long lo = (long long)w * total / G;
+    const long long hi = (long long)(w + 1) * total / G;
+    long long off;
+    int b = seq_containing<D, HB>(p, lo, off);
+    if (b >= p.B) return;
+    SeqUnits<D, HB> su;
+    su.init(p, b);
+    int h = (int)((lo - off) / su.bytes);
+    off += (long long)h * su.bytes;
+    float (*plds)[32] = plds_all[threadIdx.x >> 6];
+    while (off < hi) {
+        const int U0 = su.first_at_or_after(lo - off);
+        const int U1 = su.first_at_or_after(hi - off);
+        if (U0 < U1) run_piece<D, HB>(p, su, b, h, U0, U1, b * p.Hkv + h + w, &ctr, plds, rec);
+        off += su.bytes;
+        if (++h == p.Hkv) {
+            h = 0;
+            if (++b >= p.B) break;
+            su.init(p, b);
         }
-        if (k == 0) tile_body<16, D, HB>(p, k, bh, slot, g0, g1);
-        else if (k == 1) tile_body<4, D, HB>(p, k, bh, slot, g0, g1);
-        else tile_body<2, D, HB>(p, k, bh, slot, g0, g1);
     }
 }
 
 // Merge the piece partials (and the fp16 tail) of one (sequence, KV head)
-// into the outputs of its HB query heads.  512 threads: thread (tgi, qd)
-// owns channel quad qd and merges pieces tgi, tgi + TGR, ... online, with
-// its loads batched so that they are in flight together; a piece without
-// group blocks carries m = -inf and is skipped.
+// into the outputs of its HB query heads.  The pieces of (b, h) are those of
+// the workgroups owning its first and its last unit and every workgroup in
+// between, at records (b*Hkv + h) + w.  512 threads: thread (tgi, qd) owns
+// channel quad qd and merges pieces tgi, tgi + TGR, ... online, with its
+// loads batched so that they are in flight together.
 template <int D, int HB>
 __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
     constexpr int NT = 512;
     constexpr int QPR = D / 4;            // float4 quads per record
     constexpr int TGR = NT / QPR;         // piece groups
-    constexpr int BATCH = 4;
+    constexpr int BATCH = 2;
     __shared__ float ts[4096];            // tail scores (log2 domain)
     __shared__ float4 red_o[NT];
     __shared__ float2 red_ml[NT];
+    __shared__ int s_range[2];
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv, h = bh % p.Hkv;
     const int tid = threadIdx.x, qd = tid % QPR, tgi = tid / QPR;
-    const int npiece = split_of<D>(p, b).nw * 3;
+    if (tid < 64) {
+        int w0 = 0, np = 0;
+        const long long total = total_bytes<D, HB>(p);
+        if (total > 0) {
+            SeqUnits<D, HB> su;
+            su.init(p, b);
+            if (su.units > 0) {
+                const int G = used_workgroups(p, total);
+                const long long first = seq_offset<D, HB>(p, b) + (long long)h * su.bytes;
+                const long long last = first + su.unit_start(su.units - 1);
+                w0 = owner_of(first, total, G);
+                np = owner_of(last, total, G) - w0 + 1;
+            }
+        }
+        if (tid == 0) {
+            s_range[0] = w0;
+            s_range[1] = np;
+        }
+    }
+    __syncthreads();
+    const int w0 = s_range[0], npiece = s_range[1];
     auto rec_of = [&](int v, int hb) {
-        return p.part + (((size_t)bh * p.nt_total + v) * HB + hb) * (D + 4);
+        return p.part + ((size_t)(bh + w0 + v) * HB + hb) * (D + 4);
     };
     for (int hb = 0; hb < HB; ++hb) {
         const int hq = h * HB + hb;
@@ -625,11 +855,11 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
 }
 
 hipError_t launch_attention(const AttnParams& ap, int D, int HB, hipStream_t st) {
-    const dim3 grid(ap.nt_total / 3, ap.B * ap.Hkv);
+    const dim3 grid(ap.G);
     const dim3 cgrid(ap.B * ap.Hkv);
 #define MKV_ATTN_CASE(DD, HH)                                                          \
     if (D == DD && HB == HH) {                                                         \
-        if (ap.nt_total > 0) attn_tile_kernel<DD, HH><<<grid, 64, 0, st>>>(ap);        \
+        attn_tile_kernel<DD, HH><<<grid, 64 * kAttnWaves, 0, st>>>(ap);                \
         attn_combine_kernel<DD, HH><<<cgrid, 512, 0, st>>>(ap);                        \
     } else
     MKV_ATTN_CASE(128, 1) MKV_ATTN_CASE(128, 2) MKV_ATTN_CASE(128, 4)

@@ -54,15 +54,17 @@ struct QuantParams {
 };
 
 // ---------------------------------------------------------------- attention
+constexpr int kAttnWaves = 8;             // wavefronts per attention workgroup (2 per SIMD)
+constexpr long long kAttnMinWgBytes = 128 << 10;  // smallest byte range given to one workgroup
+
 struct AttnParams {
     const uint16_t* q;      // [B][Hq][d]
     const uint8_t* pool[3];
     int cap[3];
     const int32_t* seg_count;
     int B, Hkv, Hq, C;
-    long long per_wave;     // bytes one wavefront streams (equal-byte split)
-    int nt_total;           // partial slots per (b, h): 3 * most parts of any (b, h)
-    float* part;            // [B*Hkv][nt_total][g][d+4]: o[d], m (log2 domain), l, 0, 0
+    int G;                  // workgroups launched (the device may use fewer)
+    float* part;            // [B*Hkv + G][g][d+4]: o[d], m (log2 domain), l, 0, 0
     const uint16_t* tail_k; // [B][Hkv][tail_len][d] or NULL
     const uint16_t* tail_v;
     int tail_len;

@@ -209,10 +209,12 @@ int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T,
  *   out[b][hq] = softmax(q k^T / sqrt(d)) v
  * over every cached token of (b, h) (all segments, in any order: attention
  * does not depend on key order) plus the tail_len fp16 tokens of the tail.
- * Cached values are dequantized in registers; accumulation is fp32.  Work
- * is split over (sequence, KV head, single-bitwidth tile of groups) in one
- * launch; a second launch merges the tile partials of each (sequence, KV
- * head) with a log-sum-exp combine.
+ * Cached values are dequantized in registers; accumulation is fp32.  One
+ * launch splits the whole cache into equal byte ranges, one per workgroup,
+ * whose wavefronts take single-bitwidth work units dynamically; a second
+ * launch merges the partials of each (sequence, KV head) with a
+ * log-sum-exp combine.  Because units are handed out dynamically, the fp32
+ * summation order (not the result beyond rounding) can differ between calls.
  *
  *   q_fp16      [B][Hq][d] fp16
  *   tail_k/v    [B][Hkv][tail_len][d] fp16, or NULL when tail_len == 0

