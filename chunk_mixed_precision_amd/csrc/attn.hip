@@ -330,13 +330,30 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     for (int c = 0; c < 32; ++c) o[c] = 0.f;
 
     float sc[2 * NTH];     // this lane's key scores: half 0, then half 1
-    float pw[8];           // value weights of tokens tq + 4m (p * scale for INT-b)
-    float qp[8];           // q_j * s_j (INT-b), this group
-    float bias = 0.f;      // sum_j q_j * mn_j over this lane's channels (INT-b)
+    float pw[8];           // value weights of tokens tq + 4m: p (FP16), p * scale / 16 (INT-b)
+    float kw[8];           // key weights q_j * s_j / 16 of this lane's channels (INT-b), this group
+    float koff = 0.f;      // initial key accumulator of codes at bits 4-7: sum_j q_j mn_j - 1024 * sum_j kw_j
+    float koff64 = 0.f;    // the same for INT2 codes at bits 6-7 (weights kw/4): sum_j q_j mn_j - 256 * sum_j kw_j
+    float alpha_v = 1.f;   // softmax rescale still owed to o[] (INT-b: applied with the value offset)
     float acc[16];
 
-    // ---- online-softmax update from sc[], probabilities to the value layout
-    auto softmax_step = [&](bool valid) {
+    // INT-b codes are converted and multiplied in one v_fma_mix_f32: a code c
+    // at bits 4-5 / 4-7 (or 6-7) of an fp16 half whose other bits are 0x6400
+    // is the fp16 number 1024 + 16c (or 1024 + 64c).  With the weight w/16
+    // (w/64) the product is 64w + cw (16w + cw); the constant parts of one
+    // group are taken off the accumulator beforehand.  Keeping every code in
+    // the upper half of the 10-bit mantissa bounds the offset at 64 times
+    // the weight, so the fp32 accumulators lose at most a few bits.
+    uint32_t vmagic;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(vmagic));
+    auto lo16 = [](uint32_t y) { return (float)__builtin_bit_cast(half2_t, y).x; };
+    auto hi16 = [](uint32_t y) { return (float)__builtin_bit_cast(half2_t, y).y; };
+
+    // ---- online-softmax update from sc[], probabilities to the value layout.
+    // FP16 units rescale o[] here; INT-b units leave the factor in alpha_v
+    // for the value phase, which folds it into the offset subtraction.
+    auto softmax_step = [&](auto bits_tag, bool valid) {
+        constexpr int BITS = decltype(bits_tag)::value;
         float mloc = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 2 * NTH; ++i) {
@@ -356,8 +373,12 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
         }
         lsum = __builtin_fmaf(lsum, alpha, psum);
         pm *= alpha;
+        if constexpr (BITS == 16) {
 #pragma unroll
-        for (int c = 0; c < 32; ++c) o[c] *= alpha;
+            for (int c = 0; c < 32; ++c) o[c] *= alpha;
+        } else {
+            alpha_v = alpha;
+        }
         // slot of token t in the value layout: (t & 3) * 8 + (t >> 2)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -374,58 +395,68 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
         pw[0] = pa.x; pw[1] = pa.y; pw[2] = pa.z; pw[3] = pa.w;
         pw[4] = pb.x; pw[5] = pb.y; pw[6] = pb.z; pw[7] = pb.w;
     };
+
     // ---- INT-b pieces
     auto key_meta = [&](const uint4* m4) {           // rows: scale lo, scale hi, min lo, min hi
         const float4 s0 = as_f4(m4[0]), s1 = as_f4(m4[1]), n0 = as_f4(m4[2]), n1 = as_f4(m4[3]);
         const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         const float kmn[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
-        bias = 0.f;
+        float bias = 0.f, sw = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             bias = __builtin_fmaf(qs[e], kmn[e], bias);
-            qp[e] = qs[e] * ks[e];
+            kw[e] = qs[e] * ks[e] * 0.0625f;
+            sw += kw[e];
         }
+        koff = __builtin_fmaf(-1024.f, sw, bias);
+        koff64 = __builtin_fmaf(-256.f, sw, bias);
     };
-    auto key_half_int4 = [&](const uint4* rows) {    // 4 key-code rows of one half
+    // 4 key-code rows of one half (INT4).  Field f of word w is the code of
+    // position 8w + f; the shifts bring fields (0, 4), (1, 5), (2, 6), (3, 7)
+    // of a word to bits 4-7 of its low / high half.
+    auto key_half_int4 = [&](const uint4* rows) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = bias;
+        for (int r = 0; r < 16; ++r) acc[r] = koff;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int w = i >> 1;
             const uint32_t ws[4] = {rows[i].x, rows[i].y, rows[i].z, rows[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float qa = qp[4 * (i & 1) + e];
-                const float qb = qa * 0.0625f;
-                const uint32_t lo = ws[e] & 0x0F0F0F0Fu, hi = ws[e] & 0xF0F0F0F0u;
-                acc[8 * w + 0] = __builtin_fmaf(qa, cvt_ub<0>(lo), acc[8 * w + 0]);
-                acc[8 * w + 1] = __builtin_fmaf(qb, cvt_ub<0>(hi), acc[8 * w + 1]);
-                acc[8 * w + 2] = __builtin_fmaf(qa, cvt_ub<1>(lo), acc[8 * w + 2]);
-                acc[8 * w + 3] = __builtin_fmaf(qb, cvt_ub<1>(hi), acc[8 * w + 3]);
-                acc[8 * w + 4] = __builtin_fmaf(qa, cvt_ub<2>(lo), acc[8 * w + 4]);
-                acc[8 * w + 5] = __builtin_fmaf(qb, cvt_ub<2>(hi), acc[8 * w + 5]);
-                acc[8 * w + 6] = __builtin_fmaf(qa, cvt_ub<3>(lo), acc[8 * w + 6]);
-                acc[8 * w + 7] = __builtin_fmaf(qb, cvt_ub<3>(hi), acc[8 * w + 7]);
+                const float wq = kw[4 * (i & 1) + e];
+                const uint32_t x = ws[e];
+                const uint32_t y[4] = {((x << 4) & 0x00F000F0u) | vmagic, (x & 0x00F000F0u) | vmagic,
+                                       ((x >> 4) & 0x00F000F0u) | vmagic, ((x >> 8) & 0x00F000F0u) | vmagic};
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    acc[8 * w + f] = __builtin_fmaf(wq, lo16(y[f]), acc[8 * w + f]);
+                    acc[8 * w + 4 + f] = __builtin_fmaf(wq, hi16(y[f]), acc[8 * w + 4 + f]);
+                }
             }
         }
     };
-    auto key_half_int2 = [&](const uint4* rows) {    // 2 key-code rows of one half
+    // 2 key-code rows of one half (INT2).  Field f of the word is the code
+    // of position f; shifted copies bring fields (2s, 2s+1) and (2s+8, 2s+9)
+    // to bits 4-5 / 6-7 of the low / high half (weights w/16 and w/64).
+    auto key_half_int2 = [&](const uint4* rows) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = bias;
+        for (int r = 0; r < 16; ++r) acc[r] = (r & 1) ? koff64 : koff;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const uint32_t ws[4] = {rows[i].x, rows[i].y, rows[i].z, rows[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float q0 = qp[4 * i + e];
-                const float qm[4] = {q0, q0 * 0.25f, q0 * 0.0625f, q0 * 0.015625f};
+                const float w16 = kw[4 * i + e], w64 = w16 * 0.25f;
+                const uint32_t x = ws[e];
+                const uint32_t src[4] = {x << 4, x, x >> 4, x >> 8};
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    const uint32_t part = ws[e] & (0x03030303u << (2 * mm));
-                    acc[0 + mm] = __builtin_fmaf(qm[mm], cvt_ub<0>(part), acc[0 + mm]);
-                    acc[4 + mm] = __builtin_fmaf(qm[mm], cvt_ub<1>(part), acc[4 + mm]);
-                    acc[8 + mm] = __builtin_fmaf(qm[mm], cvt_ub<2>(part), acc[8 + mm]);
-                    acc[12 + mm] = __builtin_fmaf(qm[mm], cvt_ub<3>(part), acc[12 + mm]);
+                for (int sh = 0; sh < 4; ++sh) {
+                    const uint32_t ya = (src[sh] & 0x00300030u) | vmagic;
+                    const uint32_t yb = (src[sh] & 0x00C000C0u) | vmagic;
+                    acc[2 * sh] = __builtin_fmaf(w16, lo16(ya), acc[2 * sh]);
+                    acc[2 * sh + 8] = __builtin_fmaf(w16, hi16(ya), acc[2 * sh + 8]);
+                    acc[2 * sh + 1] = __builtin_fmaf(w64, lo16(yb), acc[2 * sh + 1]);
+                    acc[2 * sh + 9] = __builtin_fmaf(w64, hi16(yb), acc[2 * sh + 9]);
                 }
             }
         }
@@ -442,44 +473,60 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
             const float s = (m & 1) ? sm.z : sm.x;
             const float mn = (m & 1) ? sm.w : sm.y;
             pm = __builtin_fmaf(pw[m], mn, pm);
-            pw[m] *= s;
+            pw[m] = pw[m] * s * 0.0625f;
         }
     };
-    auto values_int4 = [&](const uint4* rows) {      // row m: token tq + 4m
+    // row m: token tq + 4m; word u holds channels 8u .. 8u+7 of the group
+    auto values_int4 = [&](const uint4* rows) {
+        float sw = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) sw += pw[m];
+        const float off = 1024.f * sw;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) o[c] = __builtin_fmaf(o[c], alpha_v, -off);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const uint32_t ws[4] = {rows[m].x, rows[m].y, rows[m].z, rows[m].w};
-            const float pv = pw[m], pb16 = pv * 0.0625f;
+            const float wv = pw[m];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const uint32_t lo = ws[u] & 0x0F0F0F0Fu, hi = ws[u] & 0xF0F0F0F0u;
-                o[8 * u + 0] = __builtin_fmaf(pv, cvt_ub<0>(lo), o[8 * u + 0]);
-                o[8 * u + 1] = __builtin_fmaf(pb16, cvt_ub<0>(hi), o[8 * u + 1]);
-                o[8 * u + 2] = __builtin_fmaf(pv, cvt_ub<1>(lo), o[8 * u + 2]);
-                o[8 * u + 3] = __builtin_fmaf(pb16, cvt_ub<1>(hi), o[8 * u + 3]);
-                o[8 * u + 4] = __builtin_fmaf(pv, cvt_ub<2>(lo), o[8 * u + 4]);
-                o[8 * u + 5] = __builtin_fmaf(pb16, cvt_ub<2>(hi), o[8 * u + 5]);
-                o[8 * u + 6] = __builtin_fmaf(pv, cvt_ub<3>(lo), o[8 * u + 6]);
-                o[8 * u + 7] = __builtin_fmaf(pb16, cvt_ub<3>(hi), o[8 * u + 7]);
+                const uint32_t x = ws[u];
+                const uint32_t y[4] = {((x << 4) & 0x00F000F0u) | vmagic, (x & 0x00F000F0u) | vmagic,
+                                       ((x >> 4) & 0x00F000F0u) | vmagic, ((x >> 8) & 0x00F000F0u) | vmagic};
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    o[8 * u + f] = __builtin_fmaf(wv, lo16(y[f]), o[8 * u + f]);
+                    o[8 * u + 4 + f] = __builtin_fmaf(wv, hi16(y[f]), o[8 * u + 4 + f]);
+                }
             }
         }
     };
-    auto values_int2 = [&](const uint4* rows) {      // row r: tokens t_{2r} (dwords 0,1), t_{2r+1} (2,3)
+    // row r: tokens t_{2r} (dwords 0,1), t_{2r+1} (dwords 2,3); word u holds
+    // channels 16u .. 16u+15 of the group
+    auto values_int2 = [&](const uint4* rows) {
+        float sw = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) sw += pw[m];
+        const float off16 = 1024.f * sw, off64 = 256.f * sw;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) o[c] = __builtin_fmaf(o[c], alpha_v, (c & 1) ? -off64 : -off16);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            const uint4 c = rows[m >> 1];
-            const uint32_t ws[2] = {(m & 1) ? c.z : c.x, (m & 1) ? c.w : c.y};
-            const float pv = pw[m];
-            const float pvm[4] = {pv, pv * 0.25f, pv * 0.0625f, pv * 0.015625f};
+            const uint4 cw = rows[m >> 1];
+            const uint32_t ws[2] = {(m & 1) ? cw.z : cw.x, (m & 1) ? cw.w : cw.y};
+            const float w16 = pw[m], w64 = w16 * 0.25f;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
+                const uint32_t x = ws[u];
+                const uint32_t src[4] = {x << 4, x, x >> 4, x >> 8};
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    const uint32_t part = ws[u] & (0x03030303u << (2 * mm));
-                    o[16 * u + 0 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<0>(part), o[16 * u + 0 + mm]);
-                    o[16 * u + 4 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<1>(part), o[16 * u + 4 + mm]);
-                    o[16 * u + 8 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<2>(part), o[16 * u + 8 + mm]);
-                    o[16 * u + 12 + mm] = __builtin_fmaf(pvm[mm], cvt_ub<3>(part), o[16 * u + 12 + mm]);
+                for (int sh = 0; sh < 4; ++sh) {
+                    const uint32_t ya = (src[sh] & 0x00300030u) | vmagic;
+                    const uint32_t yb = (src[sh] & 0x00C000C0u) | vmagic;
+                    o[16 * u + 2 * sh] = __builtin_fmaf(w16, lo16(ya), o[16 * u + 2 * sh]);
+                    o[16 * u + 2 * sh + 8] = __builtin_fmaf(w16, hi16(ya), o[16 * u + 2 * sh + 8]);
+                    o[16 * u + 2 * sh + 1] = __builtin_fmaf(w64, lo16(yb), o[16 * u + 2 * sh + 1]);
+                    o[16 * u + 2 * sh + 9] = __builtin_fmaf(w64, hi16(yb), o[16 * u + 2 * sh + 9]);
                 }
             }
         }
@@ -522,7 +569,7 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
             } else if (ph == 1) {
                 key_half_int4(cur);
                 take_half(1);
-                softmax_step(valid);
+                softmax_step(bits_tag, valid);
                 value_meta(cur + 4);
             } else {
                 values_int4(cur);
@@ -534,7 +581,7 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
                 take_half(0);
                 key_half_int2(cur + 6);
                 take_half(1);
-                softmax_step(valid);
+                softmax_step(bits_tag, valid);
             } else {
                 value_meta(cur);
                 values_int2(cur + 4);
@@ -547,7 +594,7 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
                     if (ph == 3) {
 #pragma unroll
                         for (int i = 0; i < 2 * NTH; ++i) sc[i] *= p.qscale;
-                        softmax_step(valid);
+                        softmax_step(bits_tag, valid);
                     }
                 }
             } else {

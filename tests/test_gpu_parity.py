@@ -250,7 +250,8 @@ def test_determinism():
     scale = o1.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
     rel = ((o1 - o2).abs() / scale).max().item()
     note(f"attention run-to-run max rel difference {rel:.2e}")
-    assert rel <= 1e-5
+    # two runs differ only in summation order; allow a tenth of the parity bar
+    assert rel <= P.ATTN_TOL / 10
 
 
 def test_workspace_reuse_across_calls():
@@ -267,7 +268,7 @@ def test_workspace_reuse_across_calls():
     torch.cuda.synchronize()
     scale = out.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
     for o in outs:
-        assert ((o - out).abs() / scale).max().item() <= 1e-5
+        assert ((o - out).abs() / scale).max().item() <= P.ATTN_TOL / 10
 
 
 def test_append_mode_tables():
