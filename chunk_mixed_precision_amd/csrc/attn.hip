@@ -158,13 +158,18 @@ struct SeqUnits {
     static constexpr long long unit_bytes(int k) { return (long long)GPI * (long long)group_bytes(bits_of_expert(k), D); }
 
     __device__ __forceinline__ void init(const AttnParams& p, int b) {
+        init_counts(p, p.seg_count[b * 3 + 0], p.seg_count[b * 3 + 1], p.seg_count[b * 3 + 2]);
+    }
+    // from the sequence's chunk counts (FP16, INT4, INT2)
+    __device__ __forceinline__ void init_counts(const AttnParams& p, int c0, int c1, int c2) {
         const int gpc = p.C / kGroup;
+        const int cnt3[3] = {c0, c1, c2};
         long long off = 0;
         int u = 0;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             // chunks beyond a pool's capacity were never written: never read them
-            const int cnt = min(max(p.seg_count[b * 3 + k], 0), p.cap[k]);
+            const int cnt = min(max(cnt3[k], 0), p.cap[k]);
             segg[k] = cnt * gpc;
             nu[k] = (segg[k] + GPI - 1) / GPI;
             ubase[k] = u;
@@ -315,6 +320,38 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     const uint8_t* seg16 = p.pool[0] + (size_t)bh * p.cap[0] * gpc * group_bytes(16, D);
     const uint8_t* seg4 = p.pool[1] + (size_t)bh * p.cap[1] * gpc * group_bytes(4, D);
     const uint8_t* seg2 = p.pool[2] + (size_t)bh * p.cap[2] * gpc * group_bytes(2, D);
+
+    // the first unit's loads go out before the query's
+    uint4 bufA[8], bufB[8];
+    auto grab = [&]() -> int {
+        int t = 0;
+        if (lane == 0) t = atomicAdd(ctr, 1);
+        return __builtin_amdgcn_readfirstlane(t);
+    };
+    // Unit U (any segment): the wave-uniform address of its first group
+    // block and this lane's offset from there (its row's block, rows past the
+    // end of the segment re-read the first block, and its 16-byte cell).
+    auto unit_addr = [&](int U, uint32_t& voff) -> const uint8_t* {
+        int k = 0, u = U;
+        const uint8_t* base = seg16;
+        uint32_t gb = (uint32_t)group_bytes(16, D);
+        if (U >= su.ubase[2]) {
+            k = 2; u = U - su.ubase[2]; base = seg2; gb = (uint32_t)group_bytes(2, D);
+        } else if (U >= su.ubase[1]) {
+            k = 1; u = U - su.ubase[1]; base = seg4; gb = (uint32_t)group_bytes(4, D);
+        }
+        const int segg = k == 0 ? su.segg[0] : (k == 1 ? su.segg[1] : su.segg[2]);
+        const bool live = u * GPI + gslot < segg;
+        voff = (live ? (uint32_t)gslot * gb : 0u) + (uint32_t)L * 16u;
+        return base + (size_t)u * GPI * gb;
+    };
+    int U = grab();
+    uint32_t vo = 0;
+    const uint8_t* ub = seg16;
+    if (U < U1) {
+        ub = unit_addr(U, vo);
+        load_rows8<D>(bufA, ub, vo, 0);
+    }
 
     // query channels 8L..8L+7 of head hq
     const uint4 qc = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + hq) * D + 8 * L);
@@ -611,29 +648,6 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     // compiler wait for every outstanding load).  Tickets are taken in
     // increasing order, so a wavefront meets the segments in the order FP16,
     // INT4, INT2 and the three loops below run once each.
-    uint4 bufA[8], bufB[8];
-    auto grab = [&]() -> int {
-        int t = 0;
-        if (lane == 0) t = atomicAdd(ctr, 1);
-        return __builtin_amdgcn_readfirstlane(t);
-    };
-    // Unit U (any segment): the wave-uniform address of its first group
-    // block and this lane's offset from there (its row's block, rows past the
-    // end of the segment re-read the first block, and its 16-byte cell).
-    auto unit_addr = [&](int U, uint32_t& voff) -> const uint8_t* {
-        int k = 0, u = U;
-        const uint8_t* base = seg16;
-        uint32_t gb = (uint32_t)group_bytes(16, D);
-        if (U >= su.ubase[2]) {
-            k = 2; u = U - su.ubase[2]; base = seg2; gb = (uint32_t)group_bytes(2, D);
-        } else if (U >= su.ubase[1]) {
-            k = 1; u = U - su.ubase[1]; base = seg4; gb = (uint32_t)group_bytes(4, D);
-        }
-        const int segg = k == 0 ? su.segg[0] : (k == 1 ? su.segg[1] : su.segg[2]);
-        const bool live = u * GPI + gslot < segg;
-        voff = (live ? (uint32_t)gslot * gb : 0u) + (uint32_t)L * 16u;
-        return base + (size_t)u * GPI * gb;
-    };
     auto run_unit = [&](auto bits_tag, auto par_tag, const uint8_t* ub, uint32_t vo, const uint8_t* ubn,
                         uint32_t von, bool valid) {
         constexpr int BITS = decltype(bits_tag)::value;
@@ -650,13 +664,6 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
         }
     };
 
-    int U = grab();
-    uint32_t vo = 0;
-    const uint8_t* ub = seg16;
-    if (U < U1) {
-        ub = unit_addr(U, vo);
-        load_rows8<D>(bufA, ub, vo, 0);
-    }
     // one step: process unit U (whose first phase is in the buffer of parity
     // PAR) and move to the next ticket; with no next unit the prefetch
     // re-reads this one
@@ -768,17 +775,49 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
     __shared__ float plds_all[kAttnWaves][64 / (D / 8)][32];
     __shared__ __align__(16) float rec[kAttnWaves * HB * (D + 4)];
     const int w = blockIdx.x;
-    const long long total = total_bytes<D, HB>(p);
+    const int lane = threadIdx.x & 63;
+    // Split.  With at most 64 sequences one pass over seg_count gives the
+    // total, the prefix offsets and this workgroup's first sequence;
+    // otherwise a second pass finds the sequence.
+    long long total, off, incl = 0, v = 0;
+    int cnt[3] = {0, 0, 0};
+    if (p.B <= 64) {
+        if (lane < p.B) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) cnt[k] = p.seg_count[lane * 3 + k];
+            SeqUnits<D, HB> sl;
+            sl.init_counts(p, cnt[0], cnt[1], cnt[2]);
+            v = sl.bytes * p.Hkv;
+        }
+        incl = v;
+#pragma unroll
+        for (int o2 = 1; o2 < 64; o2 <<= 1) {
+            const long long y = __shfl_up(incl, o2);
+            if (lane >= o2) incl += y;
+        }
+        total = uniform64(__shfl(incl, 63));
+    } else {
+        total = total_bytes<D, HB>(p);
+    }
     if (total == 0) return;
     const int G = used_workgroups(p, total);
     if (w >= G) return;
     const long long lo = (long long)w * total / G;
     const long long hi = (long long)(w + 1) * total / G;
-    long long off;
-    int b = seq_containing<D, HB>(p, lo, off);
-    if (b >= p.B) return;
+    int b;
     SeqUnits<D, HB> su;
-    su.init(p, b);
+    if (p.B <= 64) {
+        const unsigned long long hit = __ballot(lane < p.B && incl > lo);
+        b = __builtin_ctzll(hit);
+        off = uniform64(__shfl(incl - v, b));
+        su.init_counts(p, __builtin_amdgcn_readfirstlane(__shfl(cnt[0], b)),
+                       __builtin_amdgcn_readfirstlane(__shfl(cnt[1], b)),
+                       __builtin_amdgcn_readfirstlane(__shfl(cnt[2], b)));
+    } else {
+        b = seq_containing<D, HB>(p, lo, off);
+        if (b >= p.B) return;
+        su.init(p, b);
+    }
     int h = (int)((lo - off) / su.bytes);
     off += (long long)h * su.bytes;
     float (*plds)[32] = plds_all[threadIdx.x >> 6];
