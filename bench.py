@@ -2,16 +2,21 @@
 """Throughput of the chunk-adaptive mixed-precision KV path on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input
-of the named workload:
-  route   mkv_route_chunks       router GEMM (bf16 MFMA) -> vote -> freezing -> reorder
+of the named workload, one call of each:
   pack    mkv_quantize_pack_kv   K/V of every chunk -> packed FP16/INT4/INT2 segments
+  route   mkv_route_chunks       router GEMM (bf16 MFMA) -> vote -> freezing -> reorder
   attend  mkv_mixed_kv_decode_attention   one decode query per (sequence, head)
 
-Inputs are resident in HBM before timing starts.  The packed cache is kept
-in R copies (R >= 4, >= 1 GiB in total): step i packs into copy i % R and
-attends over copy (i + 1) % R, whose bytes are identical (same inputs, same
-deterministic kernels) and were written R - 1 steps earlier, so the 256 MB
-last-level cache cannot serve the attention read.
+Inputs are resident in HBM before timing starts.  The routing of the
+synthetic hidden states is the same in every step, so no call depends on
+another call of the same step.  The packed cache is kept in R copies
+(R >= 4, >= 1 GiB in total): step i packs into copy i % R and attends over
+copy (i + 1) % R, whose bytes are identical (same inputs, same deterministic
+kernels) and were written R - 1 steps earlier, so the 256 MB last-level
+cache cannot serve the attention read.  The router runs between the two so
+that the 207 MB just written by the pack (a prefill-time write that a decode
+step does not make) leaves the last-level cache while the router computes,
+not while attention reads.
 
 Prints one JSON line.  value = decode-attention effective GB/s (packed KV
 bytes + q + out per launch / attention time); the quantize rate, router rate
@@ -43,7 +48,37 @@ def parse():
     ap.add_argument("--workload", default=configs.LLAMA2_7B_32K.name, choices=[w.name for w in configs.ALL])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle timing on the host (0 disables it)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before timing, run one device-to-device copy of this many MiB (a known-size "
+                         "kernel that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+ATTN_SOURCES = ("chunk_mixed_precision_amd/csrc/attn.hip", "chunk_mixed_precision_amd/csrc/mkv_kernels.h",
+                "chunk_mixed_precision_amd/csrc/mkv_internal.h")
+
+
+def attention_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention call from committed rocprofv3 FETCH_SIZE and
+    WRITE_SIZE counts (scaled by the counts of a known-size copy), or None if
+    none were taken for this workload or the attention sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("attention_source_sha256") != attention_source_hash():
+        return None
+    return rec
 
 
 def cpu_baseline(w, k, v, q, tab_bits, budget_s):
@@ -131,6 +166,11 @@ def main():
         mkv.quantize_pack_kv(k, v, tab, c)
     ws_attn = mkv.attention_workspace(w.B, w.Hq, one, dev)
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     nev = args.steps
@@ -140,10 +180,10 @@ def main():
         e = ev[i] if rec else None
         if e:
             e[0].record()
-        mkv.route_chunks(tab, w.C, x=x, w12=w12, w3=w3, b3=b3, workspace=ws_route)
+        mkv.quantize_pack_kv(k, v, tab, caches[i % R])
         if e:
             e[1].record()
-        mkv.quantize_pack_kv(k, v, tab, caches[i % R])
+        mkv.route_chunks(tab, w.C, x=x, w12=w12, w3=w3, b3=b3, workspace=ws_route)
         if e:
             e[2].record()
         mkv.mixed_kv_decode_attention(q, caches[(i + 1) % R], out=out, workspace=ws_attn)
@@ -159,11 +199,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    t_route = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
-    t_pack = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
+    t_pack = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
+    t_route = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
     t_attn = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(nev)]) * 1e-3
 
     attn_bytes = configs.effective_attention_bytes(w, seg)
+    traffic = measured_traffic(w.name)
     pack_read = w.B * w.Hkv * w.T * w.d * 2 * 2
     pack_write = sum(int(seg[b, kk]) * configs.chunk_bytes(bits, w.d, w.C) * w.Hkv
                      for b in range(w.B) for kk, bits in enumerate(configs.EXPERT_BITS))
@@ -173,7 +214,7 @@ def main():
     avg_bits = float(sum(seg[:, kk].sum() * bits for kk, bits in enumerate(configs.EXPERT_BITS)) / seg.sum())
 
     res = {
-        "metric": "mixed-KV decode attention effective HBM GB/s (+ quantize tokens/s)",
+        "metric": "mixed-KV decode attention effective HBM GB/s (% of peak) + quantize tokens/s",
         "value": round(attn_gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -190,20 +231,30 @@ def main():
                    "chunk_mix": [int(s) for s in seg.sum(0)], "avg_bits": round(avg_bits, 3),
                    "cache_copies": R},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attention call (tile + combine launches)",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else traffic["bytes_per_call"],
+                     "kernel": "mkv_mixed_kv_decode_attention call (attn_tile_kernel + attn_combine_kernel)",
                      "bytes_per_launch": attn_bytes, "avg_launch_us": round(a_mean * 1e6, 3)},
         "quantize_tokens_per_s": round(w.B * w.T / float(t_pack.mean()), 1),
         "kernels": {
             "route": {"us": round(float(t_route.mean()) * 1e6, 2),
-                      "tflops": round(router_flop / float(t_route.mean()) / 1e12, 2),
-                      "frac_bf16_peak": round(router_flop / float(t_route.mean()) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                      "roofline": {"bound": "mfma", "achieved": round(router_flop / float(t_route.mean()) / 1e12, 2),
+                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": round(router_flop / float(t_route.mean()) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                   "flop_per_launch": router_flop}},
             "pack": {"us": round(float(t_pack.mean()) * 1e6, 2),
-                     "gbs": round((pack_read + pack_write) / float(t_pack.mean()) / 1e9, 2),
-                     "frac_hbm": round((pack_read + pack_write) / float(t_pack.mean()) / 1e9 / HBM_PEAK_GBS, 4),
-                     "bytes": pack_read + pack_write},
+                     "roofline": {"bound": "hbm", "achieved": round((pack_read + pack_write) / float(t_pack.mean()) / 1e9, 2),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round((pack_read + pack_write) / float(t_pack.mean()) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "bytes_per_launch": pack_read + pack_write}},
             "attend": {"us": round(a_mean * 1e6, 2), "us_p10": round(float(np.percentile(t_attn, 10)) * 1e6, 2),
-                       "us_p90": round(float(np.percentile(t_attn, 90)) * 1e6, 2), "bytes": attn_bytes},
+                       "us_p90": round(float(np.percentile(t_attn, 90)) * 1e6, 2), "bytes": attn_bytes,
+                       "traffic": None if traffic is None else {
+                           "bytes_per_call": traffic["bytes_per_call"],
+                           "ratio_to_algorithmic": traffic["ratio_to_algorithmic"],
+                           "fetch_factor": traffic["calibration"]["fetch_factor"],
+                           "write_factor": traffic["calibration"]["write_factor"],
+                           "source": "profiles/pmc_traffic.json"}},
         },
     }
     if args.cpu_seconds > 0:
