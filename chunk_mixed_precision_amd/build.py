@@ -27,7 +27,8 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"),
 ]
 # The quantizer must round once per operation: no contraction into FMAs.
-PER_FILE = {"quant.hip": ["-ffp-contract=off"]}
+# Its inputs are finite fp16, so min/max need no NaN quieting (no IEEE mode).
+PER_FILE = {"quant.hip": ["-ffp-contract=off", "-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def hipcc() -> str:
