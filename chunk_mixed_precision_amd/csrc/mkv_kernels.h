@@ -10,7 +10,8 @@ namespace mkv {
 // ---------------------------------------------------------------- router
 constexpr int kRouterBM = 256;   // tokens per workgroup tile
 constexpr int kRouterBI = 128;   // inner indices per workgroup tile (128 W1 + 128 W2 rows)
-constexpr int kRouterBK = 32;    // K step staged in LDS
+constexpr int kRouterBK = 64;    // K step staged in LDS
+constexpr int kRouterWaves = 8;  // wavefronts per router workgroup
 
 struct RouterParams {
     const uint16_t* x;      // [M][D] bf16 bits

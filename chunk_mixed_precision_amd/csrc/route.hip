@@ -25,51 +25,57 @@ typedef __attribute__((address_space(1))) void glob_void;
 constexpr int BM = kRouterBM;          // 256 tokens
 constexpr int BI = kRouterBI;          // 128 inner indices -> 256 W12 rows
 constexpr int BN = 2 * BI;
-constexpr int BK = kRouterBK;          // 32 bf16 = 64 B per row and stage
-constexpr int ROWB = BK * 2;           // bytes per tile row in LDS
+constexpr int BK = kRouterBK;          // K elements per LDS stage
+constexpr int NW = kRouterWaves;       // wavefronts per workgroup (2 per SIMD)
+constexpr int NT = 64 * NW;            // threads
+constexpr int ROWB = BK * 2;           // bytes per tile row and stage
+constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
 constexpr int STAGE = (BM + BN) * ROWB;   // A tile then B tile
-constexpr int LDA = BM / 2 + 1;        // epilogue: a[inner][128 tokens], padded row
+constexpr int LPS = BM * ROWB / (NT * 16);  // direct loads per thread and stage, for A (and for B)
+constexpr int LDA = BM + 1;            // epilogue: a[inner][token], padded row of floats
 constexpr int LDS_BYTES = (2 * STAGE > BI * LDA * 4) ? 2 * STAGE : BI * LDA * 4;
+static_assert(CPR == 8 && BM == BN && BM * ROWB % (NT * 16) == 0, "router tile shape");
 
-// 16-byte chunk c of tile row r sits at chunk c ^ ((r >> 1) & 3) of its
-// 64-byte LDS row: the eight rows read by one MFMA operand load then fall on
-// distinct bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3); }
+// 16-byte chunk c of tile row r sits at chunk c ^ ((r >> 1) & 7) of its
+// 128-byte LDS row: the 16 rows that one 256-byte LDS cycle of a fragment
+// load serves then fall on 16 distinct bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 }  // namespace
 
 // Router GEMM with the gate and the W3 projection fused in the epilogue.
-// Workgroup tile: 256 tokens x 128 inner indices (W1 and W2 rows of those
-// indices), K staged 32 at a time through two LDS buffers filled by
-// direct global->LDS loads.  256 threads = 4 waves as 2 (tokens) x 2 (inner);
-// wave (wm, wn) owns tokens wm*128..+127 and inner wn*64..+63: 4 x 4 MFMA
-// 32x32x16 bf16 blocks (two W1 and two W2 column blocks).  Tiles are ordered
-// so that the eight inner tiles of a token tile run on one XCD and share its
+// Workgroup tile: 256 tokens x 128 inner indices (the W1 and the W2 rows of
+// those indices), K staged 64 at a time through two LDS buffers filled by
+// direct global->LDS loads.  512 threads = 8 waves, two per SIMD so that
+// one wave's LDS fragment reads overlap the other's MFMAs: wave (wm, wn)
+// owns tokens wm*128..+127 and inner wn*32..+31, i.e. 4 x 2 MFMA 32x32x16
+// bf16 blocks (h1 and h2 of the same inner indices).  Tiles are ordered so
+// that the eight inner tiles of a token tile run on one XCD and share its
 // L2.
-__global__ __launch_bounds__(256, 1) void router_gemm_kernel(RouterParams p) {
+__global__ __launch_bounds__(NT, 2) void router_gemm_kernel(RouterParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const int NT = p.I / BI;
+    const int NTI = p.I / BI;
     const int MT = (p.M + BM - 1) / BM;
     // XCD-aware order: workgroup id -> (token tile, inner tile)
     const int id = blockIdx.x;
     const int xcd = id & 7, local = id >> 3;
-    const int mt = (local / NT) * 8 + xcd, nt = local % NT;
+    const int mt = (local / NTI) * 8 + xcd, nt = local % NTI;
     if (mt >= MT) return;
     const int m0 = mt * BM, i0 = nt * BI;
     const int D = p.D;
 
-    // this lane's source rows for its 4 + 4 direct loads per stage: load j of
-    // wave w fills LDS bytes [(4w + j) KB, +1 KB) of the A (or B) region
-    const uint16_t* a_src[4];
-    const uint16_t* b_src[4];
+    // this thread's source rows for its direct loads: load j fills LDS bytes
+    // [(j * NT + tid) * 16, +16) of the A (and of the B) region
+    const uint16_t* a_src[LPS];
+    const uint16_t* b_src[LPS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = (wave * 4 + j) * 16 + (lane >> 2);     // tile row
-        const int c = swz(r, lane & 3);                      // logical chunk held by this slot
+    for (int j = 0; j < LPS; ++j) {
+        const int r = (j * NT + tid) / CPR;                  // tile row
+        const int c = swz(r, tid % CPR);                     // logical chunk held by this slot
         const int xr = min(m0 + r, p.M - 1);                 // rows past M read a valid row
         a_src[j] = p.x + (size_t)xr * D + c * 8;
         const int wr = r < BI ? i0 + r : p.I + i0 + (r - BI);
@@ -78,19 +84,19 @@ __global__ __launch_bounds__(256, 1) void router_gemm_kernel(RouterParams p) {
     auto stage_load = [&](int buf, int k0) {
         uint8_t* base = lds + buf * STAGE;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < LPS; ++j) {
             __builtin_amdgcn_global_load_lds((glob_void*)(a_src[j] + k0),
-                                             (lds_void*)(base + (wave * 4 + j) * 1024), 16, 0, 0);
+                                             (lds_void*)(base + (j * NT + wave * 64) * 16), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((glob_void*)(b_src[j] + k0),
-                                             (lds_void*)(base + BM * ROWB + (wave * 4 + j) * 1024), 16, 0, 0);
+                                             (lds_void*)(base + BM * ROWB + (j * NT + wave * 64) * 16), 16, 0, 0);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
 
@@ -107,67 +113,69 @@ __global__ __launch_bounds__(256, 1) void router_gemm_kernel(RouterParams p) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int c = 2 * ks + lh;
-            bf16x8 af[4], bfr[4];
+            bf16x8 af[4], bfr[2];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const int r = wm * 128 + mb * 32 + lr;
                 af[mb] = *reinterpret_cast<const bf16x8*>(As + r * ROWB + swz(r, c) * 16);
             }
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const int r = (nb < 2 ? 0 : BI) + wn * 64 + (nb & 1) * 32 + lr;
+            for (int nb = 0; nb < 2; ++nb) {
+                const int r = nb * BI + wn * 32 + lr;
                 bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + r * ROWB + swz(r, c) * 16);
             }
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
+                for (int nb = 0; nb < 2; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    // ---------------- epilogue: a = SiLU(h1 * h2), then this tile's share of
-    // z = a W3^T, in two rounds of 128 tokens through LDS as a[inner][token]
+    // ---------------- epilogue: a = SiLU(h1 * h2) = u * sigmoid(u) into LDS as
+    // a[inner][token], then this tile's share of z = a W3^T: thread (half,
+    // token) sums 64 inner indices; the two halves are added in a fixed order.
     float* a_lds = reinterpret_cast<float*>(lds);
 #pragma unroll
-    for (int round = 0; round < 2; ++round) {
-        if (wm == round) {
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int tok = mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                        const int ii = wn * 64 + nb * 32 + lr;
-                        const float u = acc[mb][nb][r] * acc[mb][nb + 2][r];
-                        a_lds[ii * LDA + tok] = u / (1.0f + expf(-u));
-                    }
+        for (int r = 0; r < 16; ++r) {
+            const int tok = wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const int ii = wn * 32 + lr;
+            const float u = acc[mb][0][r] * acc[mb][1][r];
+            const float e = __builtin_amdgcn_exp2f(-u * 1.4426950408889634f);
+            a_lds[ii * LDA + tok] = u * __builtin_amdgcn_rcpf(1.0f + e);
+        }
+    __syncthreads();
+    {
+        const int tok = tid % BM;
+        const int half = __builtin_amdgcn_readfirstlane(tid / BM);      // wave-uniform
+        const float* w3 = p.w3 + i0 + half * (BI / 2);
+        float z0 = 0.f, z1 = 0.f, z2 = 0.f;
+#pragma unroll 8
+        for (int i = 0; i < BI / 2; ++i) {
+            const float a = a_lds[(half * (BI / 2) + i) * LDA + tok];
+            z0 = __builtin_fmaf(a, w3[i], z0);
+            z1 = __builtin_fmaf(a, w3[p.I + i], z1);
+            z2 = __builtin_fmaf(a, w3[2 * p.I + i], z2);
         }
         __syncthreads();
-        {
-            const int tok = tid >> 1, half = tid & 1;
-            const float* w3 = p.w3 + i0 + half * 64;
-            float z0 = 0.f, z1 = 0.f, z2 = 0.f;
-            for (int i = 0; i < 64; ++i) {
-                const float a = a_lds[(half * 64 + i) * LDA + tok];
-                z0 = __builtin_fmaf(a, w3[i], z0);
-                z1 = __builtin_fmaf(a, w3[p.I + i], z1);
-                z2 = __builtin_fmaf(a, w3[2 * p.I + i], z2);
-            }
-            // fixed order: lower half + upper half
-            const float y0 = __shfl_xor(z0, 1), y1 = __shfl_xor(z1, 1), y2 = __shfl_xor(z2, 1);
-            const int row = m0 + round * 128 + tok;
-            if (half == 0 && row < p.M) {
-                float* zp = p.zpart + ((size_t)nt * p.M + row) * 3;
-                zp[0] = z0 + y0;
-                zp[1] = z1 + y1;
-                zp[2] = z2 + y2;
-            }
+        float* zz = a_lds;                    // [BM][3] partials of the upper half
+        if (half == 1) {
+            zz[tok * 3 + 0] = z0;
+            zz[tok * 3 + 1] = z1;
+            zz[tok * 3 + 2] = z2;
         }
         __syncthreads();
+        const int row = m0 + tok;
+        if (half == 0 && row < p.M) {
+            float* zp = p.zpart + ((size_t)nt * p.M + row) * 3;
+            zp[0] = z0 + zz[tok * 3 + 0];
+            zp[1] = z1 + zz[tok * 3 + 1];
+            zp[2] = z2 + zz[tok * 3 + 2];
+        }
     }
 }
 
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(256) void reorder_kernel(ReorderParams p) {
 hipError_t launch_router(const RouterParams& rp, hipStream_t st) {
     const int MT = (rp.M + BM - 1) / BM;
     const int MT8 = (MT + 7) / 8 * 8;
-    router_gemm_kernel<<<dim3(MT8 * (rp.I / BI)), 256, 0, st>>>(rp);
+    router_gemm_kernel<<<dim3(MT8 * (rp.I / BI)), NT, 0, st>>>(rp);
     return hipGetLastError();
 }
 
