@@ -12,6 +12,7 @@ constexpr int kRouterBM = 256;   // tokens per workgroup tile
 constexpr int kRouterBI = 128;   // inner indices per workgroup tile (128 W1 + 128 W2 rows)
 constexpr int kRouterBK = 64;    // K step staged in LDS
 constexpr int kRouterWaves = 8;  // wavefronts per router workgroup
+constexpr int kRouterStages = 2; // LDS ring depth of the router GEMM
 
 struct RouterParams {
     const uint16_t* x;      // [M][D] bf16 bits

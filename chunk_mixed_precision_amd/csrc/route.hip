@@ -33,13 +33,20 @@ constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
 constexpr int STAGE = (BM + BN) * ROWB;   // A tile then B tile
 constexpr int LPS = BM * ROWB / (NT * 16);  // direct loads per thread and stage, for A (and for B)
 constexpr int LDA = BM + 1;            // epilogue: a[inner][token], padded row of floats
-constexpr int LDS_BYTES = (2 * STAGE > BI * LDA * 4) ? 2 * STAGE : BI * LDA * 4;
-static_assert(CPR == 8 && BM == BN && BM * ROWB % (NT * 16) == 0, "router tile shape");
+constexpr int NSTAGE = kRouterStages;  // LDS ring depth
+constexpr int LDS_BYTES = (NSTAGE * STAGE > BI * LDA * 4) ? NSTAGE * STAGE : BI * LDA * 4;
+static_assert((CPR == 8 || CPR == 4) && BM == BN && BM * ROWB % (NT * 16) == 0, "router tile shape");
+static_assert(NSTAGE >= 2 && (NSTAGE - 2) * 2 * LPS < 64, "vmcnt range");
 
-// 16-byte chunk c of tile row r sits at chunk c ^ ((r >> 1) & 7) of its
-// 128-byte LDS row: the 16 rows that one 256-byte LDS cycle of a fragment
+// 16-byte chunk c of tile row r sits at chunk c ^ ((r / (256 / ROWB)) % CPR)
+// of its LDS row: the 16 rows that one 256-byte LDS cycle of a fragment
 // load serves then fall on 16 distinct bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r / (256 / ROWB)) & (CPR - 1)); }
+
+// s_waitcnt immediate waiting until at most n vector memory loads are
+// outstanding (gfx9 encoding: vmcnt [3:0] and [15:14]; the other counters
+// left at their maximum).
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 }  // namespace
 
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(NT, 2) void router_gemm_kernel(RouterParams p) {
         b_src[j] = p.w12 + (size_t)wr * D + c * 8;
     }
     auto stage_load = [&](int buf, int k0) {
-        uint8_t* base = lds + buf * STAGE;
+        uint8_t* base = lds + (buf % NSTAGE) * STAGE;
 #pragma unroll
         for (int j = 0; j < LPS; ++j) {
             __builtin_amdgcn_global_load_lds((glob_void*)(a_src[j] + k0),
@@ -102,12 +109,18 @@ __global__ __launch_bounds__(NT, 2) void router_gemm_kernel(RouterParams p) {
 
     const int lr = lane & 31, lh = lane >> 5;
     const int nk = D / BK;
-    stage_load(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+    // Ring of NSTAGE LDS stages: stage s lives in buffer s % NSTAGE and is
+    // issued NSTAGE-1 iterations before it is read, into the buffer whose
+    // reads ended at the previous barrier.  A lane's loads complete in issue
+    // order, so "stage kt+1 has landed" is a bound on the loads issued after
+    // it; the barrier then makes every lane's part visible.
+    for (int st = 0; st < NSTAGE - 1 && st < nk; ++st) stage_load(st, st * BK);
+    if (nk > NSTAGE - 2) __builtin_amdgcn_s_waitcnt(wait_vm((NSTAGE - 2) * 2 * LPS));
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) stage_load(cur ^ 1, (kt + 1) * BK);
+        const int cur = kt % NSTAGE;
+        if (kt + NSTAGE - 1 < nk) stage_load(kt + NSTAGE - 1, (kt + NSTAGE - 1) * BK);
         const uint8_t* As = lds + cur * STAGE;
         const uint8_t* Bs = As + BM * ROWB;
 #pragma unroll
@@ -130,7 +143,9 @@ __global__ __launch_bounds__(NT, 2) void router_gemm_kernel(RouterParams p) {
                 for (int nb = 0; nb < 2; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(0);
+        // loads issued after stage kt+1: those of stages kt+2 .. min(kt+NSTAGE-1, nk-1)
+        if (kt + NSTAGE - 1 < nk) __builtin_amdgcn_s_waitcnt(wait_vm((NSTAGE - 2) * 2 * LPS));
+        else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
