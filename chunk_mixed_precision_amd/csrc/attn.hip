@@ -147,7 +147,7 @@ __device__ __forceinline__ long long uniform64(long long x) {
 // same segment sizes, so the geometry depends on the sequence only.
 template <int D, int HB>
 struct SeqUnits {
-    static constexpr int GPI = (512 / D) / HB;      // group blocks per unit
+    static constexpr int GPI = (512 / D) * attn_heads_per_row(HB) / HB;   // group blocks per unit
     int segg[3];        // group blocks written in each segment
     int nu[3];          // units in each segment
     int ubase[3];       // index of each segment's first unit
@@ -294,23 +294,31 @@ __device__ __forceinline__ int seq_containing(const AttnParams& p, long long x, 
 // Units [U0, U1) of the stream of (b, h), processed by the kAttnWaves
 // wavefronts of the workgroup, which take units from the ticket counter
 // *ctr.  Leaves one partial per query head of the group at record `slot`.
+//
+// A row serves HPR query heads of the KV head (one when HB = 1, two
+// otherwise): every code word is unpacked once and feeds the HPR heads'
+// FMAs.  With HB = 4 the two rows of a row pair take the same group block
+// for heads {0, 1} and {2, 3}.
 template <int D, int HB>
 __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D, HB>& su, int b, int h, int U0,
-                                          int U1, int slot, int* ctr, float (*plds)[32], float* rec) {
+                                          int U1, int slot, int* ctr, float* plds, float* rec) {
     constexpr int S = D / 8;
     constexpr int R = 64 / S;          // rows per wave
     constexpr int NG = D / 32;         // value groups per token
-    constexpr int GPI = R / HB;        // group blocks per unit
+    constexpr int HPR = attn_heads_per_row(HB);
+    constexpr int RPG = HB / HPR;      // rows per group block
+    constexpr int GPI = R / RPG;       // group blocks per unit
     constexpr int NTH = 16 / S;        // tokens per lane and key half after the reduce-scatter
     constexpr int RECF = D + 4;        // floats per merged record
+    static_assert(GPI == SeqUnits<D, HB>::GPI, "unit geometry");
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = lane / S, L = lane % S;
-    const int hb = row % HB, gslot = row / HB;
+    const int hs = row % RPG, gslot = row / RPG;
     const int G = L % NG, tq = L / NG;
     const int fx = tok_xor(S, L);
     const int bh = b * p.Hkv + h;
-    const int hq = h * HB + hb;
+    const int hq0 = h * HB + hs * HPR;   // this row's first query head
 
     if (threadIdx.x == 0) *ctr = U0;
     __syncthreads();
@@ -353,26 +361,35 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
         load_rows8<D>(bufA, ub, vo, 0);
     }
 
-    // query channels 8L..8L+7 of head hq
-    const uint4 qc = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + hq) * D + 8 * L);
-    const uint32_t qw[4] = {qc.x, qc.y, qc.z, qc.w};
-    const half2_t qh0 = as_h2(qw[0]), qh1 = as_h2(qw[1]), qh2 = as_h2(qw[2]), qh3 = as_h2(qw[3]);
-    float qs[8];           // q * log2(e)/sqrt(d) in fp32 (INT-b keys), set after the FP16 segment
-
-    float M = -INFINITY;   // running max of this row (log2 domain), row-uniform
-    float lsum = 0.f;      // this lane's share of the softmax denominator
-    float o[32];           // channels 32G .. 32G+31
-    float pm = 0.f;        // sum_t p_t * mn_t over this lane's value tokens
+    // query channels 8L..8L+7 of this row's heads
+    uint32_t qw[HPR][4];
 #pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] = 0.f;
+    for (int j = 0; j < HPR; ++j) {
+        const uint4 qc = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + hq0 + j) * D + 8 * L);
+        qw[j][0] = qc.x; qw[j][1] = qc.y; qw[j][2] = qc.z; qw[j][3] = qc.w;
+    }
+    float qs[HPR][8];      // q * log2(e)/sqrt(d) in fp32 (INT-b keys), set after the FP16 segment
 
-    float sc[2 * NTH];     // this lane's key scores: half 0, then half 1
-    float pw[8];           // value weights of tokens tq + 4m: p (FP16), p * scale / 16 (INT-b)
-    float kw[8];           // key weights q_j * s_j / 16 of this lane's channels (INT-b), this group
-    float koff = 0.f;      // initial key accumulator of codes at bits 4-7: sum_j q_j mn_j - 1024 * sum_j kw_j
-    float koff64 = 0.f;    // the same for INT2 codes at bits 6-7 (weights kw/4): sum_j q_j mn_j - 256 * sum_j kw_j
-    float alpha_v = 1.f;   // softmax rescale still owed to o[] (INT-b: applied with the value offset)
-    float acc[16];
+    float M[HPR];          // running max of this row and head (log2 domain), row-uniform
+    float lsum[HPR];       // this lane's share of the softmax denominator
+    float o[HPR][32];      // channels 32G .. 32G+31
+    float pm[HPR];         // sum_t p_t * mn_t over this lane's value tokens
+#pragma unroll
+    for (int j = 0; j < HPR; ++j) {
+        M[j] = -INFINITY;
+        lsum[j] = 0.f;
+        pm[j] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) o[j][c] = 0.f;
+    }
+
+    float sc[HPR][2 * NTH];   // this lane's key scores: half 0, then half 1
+    float pw[HPR][8];         // value weights of tokens tq + 4m: p (FP16), p * scale / 16 (INT-b)
+    float kw[HPR][8];         // key weights q_j * s_j / 16 of this lane's channels (INT-b), this group
+    float koff[HPR];          // initial key accumulator of codes at bits 4-7: sum_j q_j mn_j - 1024 * sum_j kw_j
+    float koff64[HPR];        // the same for INT2 codes at bits 6-7 (weights kw/4): sum_j q_j mn_j - 256 * sum_j kw_j
+    float alpha_v[HPR];       // softmax rescale still owed to o[] (INT-b: applied with the value offset)
+    float acc[HPR][16];
 
     // INT-b codes are converted and multiplied in one v_fma_mix_f32: a code c
     // at bits 4-5 / 4-7 (or 6-7) of an fp16 half whose other bits are 0x6400
@@ -391,46 +408,54 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     // for the value phase, which folds it into the offset subtraction.
     auto softmax_step = [&](auto bits_tag, bool valid) {
         constexpr int BITS = decltype(bits_tag)::value;
-        float mloc = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 2 * NTH; ++i) {
-            if (!valid) sc[i] = -INFINITY;
-            mloc = fmaxf(mloc, sc[i]);
-        }
-        mloc = row_max<S>(mloc);
-        const float Mn = fmaxf(M, mloc);
-        const float alpha = (Mn == -INFINITY) ? 1.f : fast_exp2(M - Mn);
-        M = Mn;
-        float pt[2 * NTH];
-        float psum = 0.f;
+        for (int j = 0; j < HPR; ++j) {
+            float mloc = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 2 * NTH; ++i) {
-            pt[i] = valid ? fast_exp2(sc[i] - Mn) : 0.f;
-            psum += pt[i];
-        }
-        lsum = __builtin_fmaf(lsum, alpha, psum);
-        pm *= alpha;
-        if constexpr (BITS == 16) {
-#pragma unroll
-            for (int c = 0; c < 32; ++c) o[c] *= alpha;
-        } else {
-            alpha_v = alpha;
-        }
-        // slot of token t in the value layout: (t & 3) * 8 + (t >> 2)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int i = 0; i < NTH; ++i) {
-                const int t = 16 * hh + (fx ^ i);
-                plds[row][(t & 3) * 8 + (t >> 2)] = pt[hh * NTH + i];
+            for (int i = 0; i < 2 * NTH; ++i) {
+                if (!valid) sc[j][i] = -INFINITY;
+                mloc = fmaxf(mloc, sc[j][i]);
             }
+            mloc = row_max<S>(mloc);
+            const float Mn = fmaxf(M[j], mloc);
+            const float alpha = (Mn == -INFINITY) ? 1.f : fast_exp2(M[j] - Mn);
+            M[j] = Mn;
+            float pt[2 * NTH];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 2 * NTH; ++i) {
+                pt[i] = valid ? fast_exp2(sc[j][i] - Mn) : 0.f;
+                psum += pt[i];
+            }
+            lsum[j] = __builtin_fmaf(lsum[j], alpha, psum);
+            pm[j] *= alpha;
+            if constexpr (BITS == 16) {
+#pragma unroll
+                for (int c = 0; c < 32; ++c) o[j][c] *= alpha;
+            } else {
+                alpha_v[j] = alpha;
+            }
+            // slot of token t in the value layout: (t & 3) * 8 + (t >> 2)
+            float* pl = plds + (row * HPR + j) * 32;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < NTH; ++i) {
+                    const int t = 16 * hh + (fx ^ i);
+                    pl[(t & 3) * 8 + (t >> 2)] = pt[hh * NTH + i];
+                }
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const float4 pa = *reinterpret_cast<const float4*>(&plds[row][tq * 8]);
-        const float4 pb = *reinterpret_cast<const float4*>(&plds[row][tq * 8 + 4]);
-        pw[0] = pa.x; pw[1] = pa.y; pw[2] = pa.z; pw[3] = pa.w;
-        pw[4] = pb.x; pw[5] = pb.y; pw[6] = pb.z; pw[7] = pb.w;
+#pragma unroll
+        for (int j = 0; j < HPR; ++j) {
+            const float* pl = plds + (row * HPR + j) * 32;
+            const float4 pa = *reinterpret_cast<const float4*>(pl + tq * 8);
+            const float4 pb = *reinterpret_cast<const float4*>(pl + tq * 8 + 4);
+            pw[j][0] = pa.x; pw[j][1] = pa.y; pw[j][2] = pa.z; pw[j][3] = pa.w;
+            pw[j][4] = pb.x; pw[j][5] = pb.y; pw[j][6] = pb.z; pw[j][7] = pb.w;
+        }
     };
 
     // ---- INT-b pieces
@@ -438,36 +463,44 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
         const float4 s0 = as_f4(m4[0]), s1 = as_f4(m4[1]), n0 = as_f4(m4[2]), n1 = as_f4(m4[3]);
         const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         const float kmn[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
-        float bias = 0.f, sw = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bias = __builtin_fmaf(qs[e], kmn[e], bias);
-            kw[e] = qs[e] * ks[e] * 0.0625f;
-            sw += kw[e];
+        for (int j = 0; j < HPR; ++j) {
+            float bias = 0.f, sw = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bias = __builtin_fmaf(qs[j][e], kmn[e], bias);
+                kw[j][e] = qs[j][e] * ks[e] * 0.0625f;
+                sw += kw[j][e];
+            }
+            koff[j] = __builtin_fmaf(-1024.f, sw, bias);
+            koff64[j] = __builtin_fmaf(-256.f, sw, bias);
         }
-        koff = __builtin_fmaf(-1024.f, sw, bias);
-        koff64 = __builtin_fmaf(-256.f, sw, bias);
     };
     // 4 key-code rows of one half (INT4).  Field f of word w is the code of
     // position 8w + f; the shifts bring fields (0, 4), (1, 5), (2, 6), (3, 7)
     // of a word to bits 4-7 of its low / high half.
     auto key_half_int4 = [&](const uint4* rows) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = koff;
+        for (int j = 0; j < HPR; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][r] = koff[j];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int w = i >> 1;
             const uint32_t ws[4] = {rows[i].x, rows[i].y, rows[i].z, rows[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float wq = kw[4 * (i & 1) + e];
                 const uint32_t x = ws[e];
                 const uint32_t y[4] = {((x << 4) & 0x00F000F0u) | vmagic, (x & 0x00F000F0u) | vmagic,
                                        ((x >> 4) & 0x00F000F0u) | vmagic, ((x >> 8) & 0x00F000F0u) | vmagic};
 #pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    acc[8 * w + f] = __builtin_fmaf(wq, lo16(y[f]), acc[8 * w + f]);
-                    acc[8 * w + 4 + f] = __builtin_fmaf(wq, hi16(y[f]), acc[8 * w + 4 + f]);
+                for (int j = 0; j < HPR; ++j) {
+                    const float wq = kw[j][4 * (i & 1) + e];
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        acc[j][8 * w + f] = __builtin_fmaf(wq, lo16(y[f]), acc[j][8 * w + f]);
+                        acc[j][8 * w + 4 + f] = __builtin_fmaf(wq, hi16(y[f]), acc[j][8 * w + 4 + f]);
+                    }
                 }
             }
         }
@@ -477,31 +510,39 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     // to bits 4-5 / 6-7 of the low / high half (weights w/16 and w/64).
     auto key_half_int2 = [&](const uint4* rows) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = (r & 1) ? koff64 : koff;
+        for (int j = 0; j < HPR; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][r] = (r & 1) ? koff64[j] : koff[j];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const uint32_t ws[4] = {rows[i].x, rows[i].y, rows[i].z, rows[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float w16 = kw[4 * i + e], w64 = w16 * 0.25f;
                 const uint32_t x = ws[e];
                 const uint32_t src[4] = {x << 4, x, x >> 4, x >> 8};
 #pragma unroll
                 for (int sh = 0; sh < 4; ++sh) {
                     const uint32_t ya = (src[sh] & 0x00300030u) | vmagic;
                     const uint32_t yb = (src[sh] & 0x00C000C0u) | vmagic;
-                    acc[2 * sh] = __builtin_fmaf(w16, lo16(ya), acc[2 * sh]);
-                    acc[2 * sh + 8] = __builtin_fmaf(w16, hi16(ya), acc[2 * sh + 8]);
-                    acc[2 * sh + 1] = __builtin_fmaf(w64, lo16(yb), acc[2 * sh + 1]);
-                    acc[2 * sh + 9] = __builtin_fmaf(w64, hi16(yb), acc[2 * sh + 9]);
+#pragma unroll
+                    for (int j = 0; j < HPR; ++j) {
+                        const float w16 = kw[j][4 * i + e], w64 = w16 * 0.25f;
+                        acc[j][2 * sh] = __builtin_fmaf(w16, lo16(ya), acc[j][2 * sh]);
+                        acc[j][2 * sh + 8] = __builtin_fmaf(w16, hi16(ya), acc[j][2 * sh + 8]);
+                        acc[j][2 * sh + 1] = __builtin_fmaf(w64, lo16(yb), acc[j][2 * sh + 1]);
+                        acc[j][2 * sh + 9] = __builtin_fmaf(w64, hi16(yb), acc[j][2 * sh + 9]);
+                    }
                 }
             }
         }
     };
     auto take_half = [&](int hh) {
-        reduce_half<S>(acc);
 #pragma unroll
-        for (int i = 0; i < NTH; ++i) sc[hh * NTH + i] = acc[i];
+        for (int j = 0; j < HPR; ++j) {
+            reduce_half<S>(acc[j]);
+#pragma unroll
+            for (int i = 0; i < NTH; ++i) sc[j][hh * NTH + i] = acc[j][i];
+        }
     };
     auto value_meta = [&](const uint4* m4) {         // (scale, min) of tokens t_{2r}, t_{2r+1}
 #pragma unroll
@@ -509,31 +550,40 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
             const float4 sm = as_f4(m4[m >> 1]);
             const float s = (m & 1) ? sm.z : sm.x;
             const float mn = (m & 1) ? sm.w : sm.y;
-            pm = __builtin_fmaf(pw[m], mn, pm);
-            pw[m] = pw[m] * s * 0.0625f;
+#pragma unroll
+            for (int j = 0; j < HPR; ++j) {
+                pm[j] = __builtin_fmaf(pw[j][m], mn, pm[j]);
+                pw[j][m] = pw[j][m] * s * 0.0625f;
+            }
         }
     };
     // row m: token tq + 4m; word u holds channels 8u .. 8u+7 of the group
     auto values_int4 = [&](const uint4* rows) {
-        float sw = 0.f;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) sw += pw[m];
-        const float off = 1024.f * sw;
+        for (int j = 0; j < HPR; ++j) {
+            float sw = 0.f;
 #pragma unroll
-        for (int c = 0; c < 32; ++c) o[c] = __builtin_fmaf(o[c], alpha_v, -off);
+            for (int m = 0; m < 8; ++m) sw += pw[j][m];
+            const float off = 1024.f * sw;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) o[j][c] = __builtin_fmaf(o[j][c], alpha_v[j], -off);
+        }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const uint32_t ws[4] = {rows[m].x, rows[m].y, rows[m].z, rows[m].w};
-            const float wv = pw[m];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t x = ws[u];
                 const uint32_t y[4] = {((x << 4) & 0x00F000F0u) | vmagic, (x & 0x00F000F0u) | vmagic,
                                        ((x >> 4) & 0x00F000F0u) | vmagic, ((x >> 8) & 0x00F000F0u) | vmagic};
 #pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    o[8 * u + f] = __builtin_fmaf(wv, lo16(y[f]), o[8 * u + f]);
-                    o[8 * u + 4 + f] = __builtin_fmaf(wv, hi16(y[f]), o[8 * u + 4 + f]);
+                for (int j = 0; j < HPR; ++j) {
+                    const float wv = pw[j][m];
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        o[j][8 * u + f] = __builtin_fmaf(wv, lo16(y[f]), o[j][8 * u + f]);
+                        o[j][8 * u + 4 + f] = __builtin_fmaf(wv, hi16(y[f]), o[j][8 * u + 4 + f]);
+                    }
                 }
             }
         }
@@ -541,17 +591,19 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     // row r: tokens t_{2r} (dwords 0,1), t_{2r+1} (dwords 2,3); word u holds
     // channels 16u .. 16u+15 of the group
     auto values_int2 = [&](const uint4* rows) {
-        float sw = 0.f;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) sw += pw[m];
-        const float off16 = 1024.f * sw, off64 = 256.f * sw;
+        for (int j = 0; j < HPR; ++j) {
+            float sw = 0.f;
 #pragma unroll
-        for (int c = 0; c < 32; ++c) o[c] = __builtin_fmaf(o[c], alpha_v, (c & 1) ? -off64 : -off16);
+            for (int m = 0; m < 8; ++m) sw += pw[j][m];
+            const float off16 = 1024.f * sw, off64 = 256.f * sw;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) o[j][c] = __builtin_fmaf(o[j][c], alpha_v[j], (c & 1) ? -off64 : -off16);
+        }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const uint4 cw = rows[m >> 1];
             const uint32_t ws[2] = {(m & 1) ? cw.z : cw.x, (m & 1) ? cw.w : cw.y};
-            const float w16 = pw[m], w64 = w16 * 0.25f;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const uint32_t x = ws[u];
@@ -560,10 +612,14 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
                 for (int sh = 0; sh < 4; ++sh) {
                     const uint32_t ya = (src[sh] & 0x00300030u) | vmagic;
                     const uint32_t yb = (src[sh] & 0x00C000C0u) | vmagic;
-                    o[16 * u + 2 * sh] = __builtin_fmaf(w16, lo16(ya), o[16 * u + 2 * sh]);
-                    o[16 * u + 2 * sh + 8] = __builtin_fmaf(w16, hi16(ya), o[16 * u + 2 * sh + 8]);
-                    o[16 * u + 2 * sh + 1] = __builtin_fmaf(w64, lo16(yb), o[16 * u + 2 * sh + 1]);
-                    o[16 * u + 2 * sh + 9] = __builtin_fmaf(w64, hi16(yb), o[16 * u + 2 * sh + 9]);
+#pragma unroll
+                    for (int j = 0; j < HPR; ++j) {
+                        const float w16 = pw[j][m], w64 = w16 * 0.25f;
+                        o[j][16 * u + 2 * sh] = __builtin_fmaf(w16, lo16(ya), o[j][16 * u + 2 * sh]);
+                        o[j][16 * u + 2 * sh + 8] = __builtin_fmaf(w16, hi16(ya), o[j][16 * u + 2 * sh + 8]);
+                        o[j][16 * u + 2 * sh + 1] = __builtin_fmaf(w64, lo16(yb), o[j][16 * u + 2 * sh + 1]);
+                        o[j][16 * u + 2 * sh + 9] = __builtin_fmaf(w64, hi16(yb), o[j][16 * u + 2 * sh + 9]);
+                    }
                 }
             }
         }
@@ -573,27 +629,32 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     auto keys_fp16 = [&](const uint4* rows, int r0) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            float a = __builtin_amdgcn_fdot2(as_h2(rows[r].x), qh0, 0.f, false);
-            a = __builtin_amdgcn_fdot2(as_h2(rows[r].y), qh1, a, false);
-            a = __builtin_amdgcn_fdot2(as_h2(rows[r].z), qh2, a, false);
-            a = __builtin_amdgcn_fdot2(as_h2(rows[r].w), qh3, a, false);
-            acc[r0 + r] = a;
+#pragma unroll
+            for (int j = 0; j < HPR; ++j) {
+                float a = __builtin_amdgcn_fdot2(as_h2(rows[r].x), as_h2(qw[j][0]), 0.f, false);
+                a = __builtin_amdgcn_fdot2(as_h2(rows[r].y), as_h2(qw[j][1]), a, false);
+                a = __builtin_amdgcn_fdot2(as_h2(rows[r].z), as_h2(qw[j][2]), a, false);
+                a = __builtin_amdgcn_fdot2(as_h2(rows[r].w), as_h2(qw[j][3]), a, false);
+                acc[j][r0 + r] = a;
+            }
         }
     };
     auto values_fp16 = [&](const uint4* rows, int mbase) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float pr = pw[mbase + (r >> 2)];
             const int cb = 8 * (r & 3);
             const uint32_t ws[4] = {rows[r].x, rows[r].y, rows[r].z, rows[r].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                o[cb + 2 * e] = __builtin_fmaf(pr, lo_h(ws[e]), o[cb + 2 * e]);
-                o[cb + 2 * e + 1] = __builtin_fmaf(pr, hi_h(ws[e]), o[cb + 2 * e + 1]);
+            for (int j = 0; j < HPR; ++j) {
+                const float pr = pw[j][mbase + (r >> 2)];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[j][cb + 2 * e] = __builtin_fmaf(pr, lo_h(ws[e]), o[j][cb + 2 * e]);
+                    o[j][cb + 2 * e + 1] = __builtin_fmaf(pr, hi_h(ws[e]), o[j][cb + 2 * e + 1]);
+                }
             }
         }
     };
-
 
     // one phase's arithmetic on the rows in `cur`
     auto compute_phase = [&](auto bits_tag, int ph, const uint4* cur, bool valid) {
@@ -630,7 +691,9 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
                     take_half(ph >> 1);
                     if (ph == 3) {
 #pragma unroll
-                        for (int i = 0; i < 2 * NTH; ++i) sc[i] *= p.qscale;
+                        for (int j = 0; j < HPR; ++j)
+#pragma unroll
+                            for (int i = 0; i < 2 * NTH; ++i) sc[j][i] *= p.qscale;
                         softmax_step(bits_tag, valid);
                     }
                 }
@@ -686,10 +749,12 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     }
     // the FP16 keys used the raw fp16 query; the INT-b keys take fp32 weights
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        qs[2 * e] = lo_h(qw[e]) * p.qscale;
-        qs[2 * e + 1] = hi_h(qw[e]) * p.qscale;
-    }
+    for (int j = 0; j < HPR; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qs[j][2 * e] = lo_h(qw[j][e]) * p.qscale;
+            qs[j][2 * e + 1] = hi_h(qw[j][e]) * p.qscale;
+        }
     {   // INT4 (odd phase count: parity flips every unit, so units go in pairs)
         const int end = min(U1, su.ubase[1] + su.nu[1]);
         bool flipped = false;
@@ -709,38 +774,40 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
         while (U < end) step(std::integral_constant<int, 2>{}, I0{}, 2, su.segg[2], su.ubase[2]);
     }
 
-    // ---------------- merge rows of the same head, then lanes of the same value group
+    // ---------------- merge rows of the same heads, then lanes of the same value group
 #pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] += pm;
-    float Mx = M;
+    for (int j = 0; j < HPR; ++j) {
 #pragma unroll
-    for (int off = S * HB; off < 64; off <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, off));
-    const float rs = (M == -INFINITY) ? 0.f : fast_exp2(M - Mx);
-    lsum *= rs;
+        for (int c = 0; c < 32; ++c) o[j][c] += pm[j];
+        float Mx = M[j];
 #pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] *= rs;
+        for (int off = S * RPG; off < 64; off <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, off));
+        const float rs = (M[j] == -INFINITY) ? 0.f : fast_exp2(M[j] - Mx);
+        float l = lsum[j] * rs;
 #pragma unroll
-    for (int off = 1; off < S; off <<= 1) lsum += __shfl_xor(lsum, off);
+        for (int off = 1; off < S; off <<= 1) l += __shfl_xor(l, off);
 #pragma unroll
-    for (int off = S * HB; off < 64; off <<= 1) lsum += __shfl_xor(lsum, off);
+        for (int off = S * RPG; off < 64; off <<= 1) l += __shfl_xor(l, off);
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-        float v = o[c];
+        for (int c = 0; c < 32; ++c) {
+            float v = o[j][c] * rs;
 #pragma unroll
-        for (int off = NG; off < S; off <<= 1) v += __shfl_xor(v, off);
+            for (int off = NG; off < S; off <<= 1) v += __shfl_xor(v, off);
 #pragma unroll
-        for (int off = S * HB; off < 64; off <<= 1) v += __shfl_xor(v, off);
-        o[c] = v;
-    }
-    // ---------------- merge the wavefronts of the workgroup in LDS
-    if (row == hb && tq == 0) {
-        float* r = rec + ((size_t)wave * HB + hb) * RECF;
-        float4* o4 = reinterpret_cast<float4*>(r + 32 * G);
+            for (int off = S * RPG; off < 64; off <<= 1) v += __shfl_xor(v, off);
+            o[j][c] = v;
+        }
+        // ---------------- the wavefront's record of head hs*HPR + j, for the workgroup merge
+        if (row == hs && tq == 0) {
+            float* r = rec + ((size_t)wave * HB + hs * HPR + j) * RECF;
+            float4* o4 = reinterpret_cast<float4*>(r + 32 * G);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o4[c] = make_float4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
-        if (G == 0) {
-            r[D] = Mx;
-            r[D + 1] = lsum;
+            for (int c = 0; c < 8; ++c)
+                o4[c] = make_float4(o[j][4 * c], o[j][4 * c + 1], o[j][4 * c + 2], o[j][4 * c + 3]);
+            if (G == 0) {
+                r[D] = Mx;
+                r[D + 1] = l;
+            }
         }
     }
     __syncthreads();
@@ -772,7 +839,7 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
 template <int D, int HB>
 __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_kernel(AttnParams p) {
     __shared__ int ctr;
-    __shared__ float plds_all[kAttnWaves][64 / (D / 8)][32];
+    __shared__ float plds_all[kAttnWaves][(64 / (D / 8)) * attn_heads_per_row(HB) * 32];
     __shared__ __align__(16) float rec[kAttnWaves * HB * (D + 4)];
     const int w = blockIdx.x;
     const int lane = threadIdx.x & 63;
@@ -820,7 +887,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
     }
     int h = (int)((lo - off) / su.bytes);
     off += (long long)h * su.bytes;
-    float (*plds)[32] = plds_all[threadIdx.x >> 6];
+    float* plds = plds_all[threadIdx.x >> 6];
     while (off < hi) {
         const int U0 = su.first_at_or_after(lo - off);
         const int U1 = su.first_at_or_after(hi - off);

@@ -58,6 +58,9 @@ struct QuantParams {
 // ---------------------------------------------------------------- attention
 constexpr int kAttnWaves = 8;             // wavefronts per attention workgroup (2 per SIMD)
 constexpr long long kAttnMinWgBytes = 128 << 10;  // smallest byte range given to one workgroup
+// Query heads served by one row of lanes: with grouped-query attention a row
+// serves two heads of its KV head, so each code word is unpacked once for both.
+constexpr int attn_heads_per_row(int hb) { return hb == 1 ? 1 : 2; }
 
 struct AttnParams {
     const uint16_t* q;      // [B][Hq][d]
