@@ -21,10 +21,10 @@ inline int hip_status(hipError_t e) {
 }
 
 // Attention work split: persistent workgroups of mkv::kAttnWaves wavefronts,
-// one per CU (256 on MI355X), each taking an equal byte range of the cache;
-// fewer when the cache at capacity is small (every range at least
-// mkv::kAttnMinWgBytes).  The device recomputes the split from the actual
-// segment counts and may use fewer still.  Partials: one record per
+// one per CU (256 on MI355X), each taking an equal cost range of the cache;
+// fewer when the cache at capacity is small (here counted in bytes: every
+// range at least mkv::kAttnMinWgCost).  The device recomputes the split from
+// the actual segment counts and unit costs and never uses more than this.  Partials: one record per
 // (sequence, head) plus one per workgroup boundary.
 constexpr long long kAttnWorkgroups = 256;
 
@@ -33,7 +33,7 @@ inline int attn_workgroups(int B, int Hkv, int d, const int* cap, int C) {
     long long bh_bytes = 0;
     for (int k = 0; k < 3; ++k) bh_bytes += (long long)cap[k] * (C / mkv::kGroup) * (long long)mkv::group_bytes(bits[k], d);
     const long long total = bh_bytes * B * Hkv;
-    long long g = total / mkv::kAttnMinWgBytes;
+    long long g = total / mkv::kAttnMinWgCost;
     if (g > kAttnWorkgroups) g = kAttnWorkgroups;
     if (g < 1) g = 1;
     return (int)g;
@@ -190,6 +190,17 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq, const mkv_cache* c
     if ((long)cache->B * Hq > 2147483647L) return MKV_ERR_UNSUPPORTED;
     if (tail_len < 0 || tail_len >= 4096) return MKV_ERR_ARG;
     if (tail_len > 0 && (!tail_k_fp16 || !tail_v_fp16)) return MKV_ERR_ARG;
+    {   // the work split counts the cost of the whole cache at capacity in 32-bit granules
+        const int gpi = (512 / cache->d) * mkv::attn_heads_per_row(g) / g;   // group blocks per unit
+        const int bits[3] = {16, 4, 2};
+        long long gran = 0;
+        for (int k = 0; k < 3; ++k) {
+            const long long units = ((long long)cache->cap[k] * (cache->C / mkv::kGroup) + gpi - 1) / gpi;
+            gran += units * ((long long)gpi * mkv::group_bytes(bits[k], cache->d) * mkv::attn_cost16(g, k) /
+                             (16 * mkv::kAttnGranule));
+        }
+        if (gran * cache->B * cache->Hkv > mkv::kAttnMaxGranules) return MKV_ERR_UNSUPPORTED;
+    }
     const size_t need = mkv_workspace_bytes(MKV_OP_ATTENTION, cache->B, Hq, cache->Hkv, cache->d, cache->C, cache->cap);
     if (!workspace || !aligned16(workspace) || workspace_bytes < need) return MKV_ERR_WORKSPACE;
 

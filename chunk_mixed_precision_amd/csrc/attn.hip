@@ -7,8 +7,10 @@
 // Work.  The packed bytes of each (sequence, KV head) -- its FP16, INT4 and
 // INT2 segments in that order -- are cut into units of one wavefront
 // iteration (GPI group blocks of one segment).  All (sequence, head) streams
-// are laid end to end and split into equal byte ranges, one per workgroup of
-// kAttnWaves wavefronts (one CU's worth); a range may span several
+// are laid end to end and split into ranges of equal cost, one per workgroup
+// of kAttnWaves wavefronts (one CU's worth); a unit's cost is its bytes times
+// a per-bitwidth weight, because an INT2 byte holds more codes to dequantize
+// than an INT4 byte and an FP16 byte fewer.  A range may span several
 // (sequence, head) streams, each giving one "piece".  Inside a piece the
 // wavefronts take units from a workgroup-local ticket counter in LDS, so a
 // wavefront that the CU's scheduler favours simply takes more units and all
@@ -18,17 +20,18 @@
 // second launch merges the partials of each (sequence, head).
 //
 // A wavefront is split into R = 64/S rows of S = d/8 lanes; each row handles
-// one group block per iteration (GQA: the rows of one iteration take the
-// same group for different query heads).  Inside a row, lane slot L owns
-// channels 8L..8L+7 of the keys and value group L % (d/32) of tokens
-// L / (d/32) + 4m.
+// one group block per iteration for one query head, or for two with
+// grouped-query attention (with four heads per KV head, two rows share a
+// group block).  Inside a row, lane slot L owns channels 8L..8L+7 of the keys
+// and value group L % (d/32) of tokens L / (d/32) + 4m.
 //
 // Scores: s_t = sum_j q_j * (code_tj * s_j + mn_j) is evaluated as
 // sum_j (q_j s_j) code_tj + sum_j q_j mn_j, so key dequantization costs one
-// FMA per code.  Codes are unpacked with v_cvt_f32_ubyteN on masked words,
-// and scale factors of 16 / 4^m are folded into the per-channel weights.
-// Per-row partial sums are combined with a select-free DPP reduce-scatter
-// (the layout's per-lane token xor makes every butterfly step keep the low
+// FMA per code and head: a masked code field ORed into an fp16 exponent
+// pattern is converted and multiplied in one v_fma_mix_f32, and the
+// pattern's constant is taken off the accumulator once per group.  Per-row
+// partial sums are combined with a select-free DPP reduce-scatter (the
+// layout's per-lane token xor makes every butterfly step keep the low
 // registers).  Values: o_j = sum_t (p_t s_t) code_tj + sum_t p_t mn_t.
 // Everything accumulates in fp32; softmax is online, in the log2 domain.
 #include "mkv_internal.h"
@@ -151,11 +154,18 @@ struct SeqUnits {
     int segg[3];        // group blocks written in each segment
     int nu[3];          // units in each segment
     int ubase[3];       // index of each segment's first unit
-    long long soff[3];  // byte offset of each segment's first unit in the stream
-    long long bytes;    // bytes of the whole stream (units x unit bytes)
+    int soff[3];        // cost offset of each segment's first unit in the stream
+    int cost;           // cost of the whole stream (units x unit cost)
     int units;
 
-    static constexpr long long unit_bytes(int k) { return (long long)GPI * (long long)group_bytes(bits_of_expert(k), D); }
+    // Cost of one unit of segment k, in granules of kAttnGranule bytes.
+    static constexpr int unit_cost(int k) {
+        return GPI * group_bytes(bits_of_expert(k), D) * attn_cost16(HB, k) / (16 * kAttnGranule);
+    }
+    static_assert(GPI * group_bytes(16, D) * attn_cost16(HB, 0) % (16 * kAttnGranule) == 0 &&
+                  GPI * group_bytes(4, D) * attn_cost16(HB, 1) % (16 * kAttnGranule) == 0 &&
+                  GPI * group_bytes(2, D) * attn_cost16(HB, 2) % (16 * kAttnGranule) == 0,
+                  "unit costs are whole granules");
 
     __device__ __forceinline__ void init(const AttnParams& p, int b) {
         init_counts(p, p.seg_count[b * 3 + 0], p.seg_count[b * 3 + 1], p.seg_count[b * 3 + 2]);
@@ -164,7 +174,7 @@ struct SeqUnits {
     __device__ __forceinline__ void init_counts(const AttnParams& p, int c0, int c1, int c2) {
         const int gpc = p.C / kGroup;
         const int cnt3[3] = {c0, c1, c2};
-        long long off = 0;
+        int off = 0;
         int u = 0;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -175,116 +185,126 @@ struct SeqUnits {
             ubase[k] = u;
             soff[k] = off;
             u += nu[k];
-            off += (long long)nu[k] * unit_bytes(k);
+            off += nu[k] * unit_cost(k);
         }
         units = u;
-        bytes = off;
+        cost = off;
     }
 
-    // Index of the first unit whose first byte is at or after stream offset x
+    // Index of the first unit whose start is at or after stream offset x
     // (units when there is none).
-    __device__ __forceinline__ int first_at_or_after(long long x) const {
+    __device__ __forceinline__ int first_at_or_after(int x) const {
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             if (nu[k] == 0) continue;
-            const long long rel = x - soff[k];
-            const long long u = rel <= 0 ? 0 : (rel + unit_bytes(k) - 1) / unit_bytes(k);
-            if (u < nu[k]) return ubase[k] + (int)u;
+            const int rel = x - soff[k];
+            const int u = rel <= 0 ? 0 : (int)(((unsigned)rel + unit_cost(k) - 1) / (unsigned)unit_cost(k));
+            if (u < nu[k]) return ubase[k] + u;
         }
         return units;
     }
 
-    __device__ __forceinline__ long long unit_start(int U) const {
-        if (U < ubase[1]) return soff[0] + (long long)(U - ubase[0]) * unit_bytes(0);
-        if (U < ubase[2]) return soff[1] + (long long)(U - ubase[1]) * unit_bytes(1);
-        return soff[2] + (long long)(U - ubase[2]) * unit_bytes(2);
+    __device__ __forceinline__ int unit_start(int U) const {
+        if (U < ubase[1]) return soff[0] + (U - ubase[0]) * unit_cost(0);
+        if (U < ubase[2]) return soff[1] + (U - ubase[1]) * unit_cost(1);
+        return soff[2] + (U - ubase[2]) * unit_cost(2);
     }
 };
 
-// Bytes of the whole cache (every (sequence, head) stream), computed by one
+// Cost of the whole cache (every (sequence, head) stream), computed by one
 // wavefront with one sequence per lane; every lane gets the result.
 template <int D, int HB>
-__device__ __forceinline__ long long total_bytes(const AttnParams& p) {
+__device__ __forceinline__ int total_cost(const AttnParams& p) {
     const int lane = threadIdx.x & 63;
-    long long t = 0;
+    int t = 0;
     for (int b0 = 0; b0 < p.B; b0 += 64) {
         const int b = b0 + lane;
-        long long x = 0;
+        int x = 0;
         if (b < p.B) {
             SeqUnits<D, HB> su;
             su.init(p, b);
-            x = su.bytes;
+            x = su.cost;
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
         t += x;
     }
-    return uniform64(t * p.Hkv);
+    return __builtin_amdgcn_readfirstlane(t * p.Hkv);
 }
 
 // Workgroups actually used: at most G, and few enough that every range is at
-// least kAttnMinWgBytes long (longer than any unit, so each workgroup
+// least kAttnMinWgCost long (longer than any unit, so each workgroup
 // between the first and the last owner of a stream owns a unit of it).
-__device__ __forceinline__ int used_workgroups(const AttnParams& p, long long total) {
-    const long long g = total / kAttnMinWgBytes;
-    return (int)max(1LL, min((long long)p.G, g));
+__device__ __forceinline__ int used_workgroups(const AttnParams& p, int total) {
+    const int g = total / (int)(kAttnMinWgCost / kAttnGranule);
+    return max(1, min(p.G, g));
 }
 
-// The workgroup whose byte range contains global offset x:
-// range w = [floor(w*T/G), floor((w+1)*T/G)).
-__device__ __forceinline__ int owner_of(long long x, long long total, int G) {
-    return (int)(((x + 1) * (long long)G - 1) / total);
+// Start of workgroup w's range, floor(w*T/G).  In fp64: the product is
+// exact (below 2^40) and the correctly rounded quotient of two such numbers
+// never crosses an integer (a non-integer quotient below 2^31 lies at least
+// 1/G from one), so the floor is exact -- and much cheaper than a 64-bit
+// integer division.
+__device__ __forceinline__ int split_point(int w, int total, int G) {
+    return (int)(((double)w * (double)total) / (double)G);
+}
+
+// The workgroup whose cost range contains global offset x:
+// range w = [floor(w*T/G), floor((w+1)*T/G)), i.e. floor(((x+1)*G - 1) / T)
+// (exact in fp64 as above).
+__device__ __forceinline__ int owner_of(int x, int total, int G) {
+    return (int)(((double)(x + 1) * (double)G - 1.0) / (double)total);
 }
 
 // Global offset of sequence b's first stream (head 0): Hkv * sum of the
-// stream bytes of sequences 0 .. b-1.  One wavefront, every lane gets it.
+// stream costs of sequences 0 .. b-1.  One wavefront, every lane gets it.
 template <int D, int HB>
-__device__ __forceinline__ long long seq_offset(const AttnParams& p, int b) {
+__device__ __forceinline__ int seq_offset(const AttnParams& p, int b) {
     const int lane = threadIdx.x & 63;
-    long long t = 0;
+    int t = 0;
     for (int b0 = 0; b0 < b; b0 += 64) {
         const int bb = b0 + lane;
-        long long x = 0;
+        int x = 0;
         if (bb < b) {
             SeqUnits<D, HB> su;
             su.init(p, bb);
-            x = su.bytes;
+            x = su.cost;
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
         t += x;
     }
-    return uniform64(t * p.Hkv);
+    return __builtin_amdgcn_readfirstlane(t * p.Hkv);
 }
 
 // The sequence whose streams contain global offset x (x < total), and the
 // global offset of its first stream.  One wavefront, uniform result.
 template <int D, int HB>
-__device__ __forceinline__ int seq_containing(const AttnParams& p, long long x, long long& seq_off) {
+__device__ __forceinline__ int seq_containing(const AttnParams& p, int x, int& seq_off) {
     const int lane = threadIdx.x & 63;
-    long long carry = 0;
+    int carry = 0;
     for (int b0 = 0; b0 < p.B; b0 += 64) {
         const int b = b0 + lane;
-        long long v = 0;
+        int v = 0;
         if (b < p.B) {
             SeqUnits<D, HB> su;
             su.init(p, b);
-            v = su.bytes * p.Hkv;
+            v = su.cost * p.Hkv;
         }
         // inclusive prefix over the lanes
-        long long incl = v;
+        int incl = v;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const long long y = __shfl_up(incl, off);
+            const int y = __shfl_up(incl, off);
             if (lane >= off) incl += y;
         }
         const unsigned long long hit = __ballot(b < p.B && carry + incl > x);
         if (hit) {
             const int l = __builtin_ctzll(hit);
-            seq_off = uniform64(carry + __shfl(incl - v, l));
+            seq_off = __builtin_amdgcn_readfirstlane(carry + __shfl(incl - v, l));
             return b0 + l;
         }
-        carry = uniform64(carry + __shfl(incl, 63));
+        carry = __builtin_amdgcn_readfirstlane(carry + __shfl(incl, 63));
     }
     seq_off = carry;
     return p.B;
@@ -293,7 +313,11 @@ __device__ __forceinline__ int seq_containing(const AttnParams& p, long long x, 
 // ---------------------------------------------------------------- one piece
 // Units [U0, U1) of the stream of (b, h), processed by the kAttnWaves
 // wavefronts of the workgroup, which take units from the ticket counter
-// *ctr.  Leaves one partial per query head of the group at record `slot`.
+// *ctr: ticket t is unit U0 + (t - tbase).  The counter is never reset: a
+// piece consumes exactly (U1 - U0) + kAttnWaves tickets (one per unit and
+// one failing grab per wavefront), all before the workgroup barrier that
+// ends the piece, so the caller knows the next piece's base.  Leaves one
+// partial per query head of the group at record `slot`.
 //
 // A row serves HPR query heads of the KV head (one when HB = 1, two
 // otherwise): every code word is unpacked once and feeds the HPR heads'
@@ -301,7 +325,7 @@ __device__ __forceinline__ int seq_containing(const AttnParams& p, long long x, 
 // for heads {0, 1} and {2, 3}.
 template <int D, int HB>
 __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D, HB>& su, int b, int h, int U0,
-                                          int U1, int slot, int* ctr, float* plds, float* rec) {
+                                          int U1, int tbase, int slot, int* ctr, float* plds, float* rec) {
     constexpr int S = D / 8;
     constexpr int R = 64 / S;          // rows per wave
     constexpr int NG = D / 32;         // value groups per token
@@ -320,9 +344,6 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     const int bh = b * p.Hkv + h;
     const int hq0 = h * HB + hs * HPR;   // this row's first query head
 
-    if (threadIdx.x == 0) *ctr = U0;
-    __syncthreads();
-
     // segment base pointers of this (b, h)
     const size_t gpc = (size_t)(p.C / kGroup);
     const uint8_t* seg16 = p.pool[0] + (size_t)bh * p.cap[0] * gpc * group_bytes(16, D);
@@ -334,7 +355,7 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     auto grab = [&]() -> int {
         int t = 0;
         if (lane == 0) t = atomicAdd(ctr, 1);
-        return __builtin_amdgcn_readfirstlane(t);
+        return U0 + (__builtin_amdgcn_readfirstlane(t) - tbase);
     };
     // Unit U (any segment): the wave-uniform address of its first group
     // block and this lane's offset from there (its row's block, rows past the
@@ -831,9 +852,9 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
 
 }  // namespace
 
-// Persistent workgroups of kAttnWaves wavefronts.  Workgroup w takes the byte
+// Persistent workgroups of kAttnWaves wavefronts.  Workgroup w takes the cost
 // range [w*T/G, (w+1)*T/G) of the end-to-end (sequence, head) streams (T
-// bytes in all) and, for every stream whose unit starts fall in it, runs
+// in all) and, for every stream whose unit starts fall in it, runs
 // those units as one piece and leaves the piece's partial at record
 // (sequence*Hkv + head) + w.
 template <int D, int HB>
@@ -843,10 +864,12 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
     __shared__ __align__(16) float rec[kAttnWaves * HB * (D + 4)];
     const int w = blockIdx.x;
     const int lane = threadIdx.x & 63;
+    if (threadIdx.x == 0) ctr = 0;
+    __syncthreads();
     // Split.  With at most 64 sequences one pass over seg_count gives the
     // total, the prefix offsets and this workgroup's first sequence;
     // otherwise a second pass finds the sequence.
-    long long total, off, incl = 0, v = 0;
+    int total, off, incl = 0, v = 0;
     int cnt[3] = {0, 0, 0};
     if (p.B <= 64) {
         if (lane < p.B) {
@@ -854,29 +877,29 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
             for (int k = 0; k < 3; ++k) cnt[k] = p.seg_count[lane * 3 + k];
             SeqUnits<D, HB> sl;
             sl.init_counts(p, cnt[0], cnt[1], cnt[2]);
-            v = sl.bytes * p.Hkv;
+            v = sl.cost * p.Hkv;
         }
         incl = v;
 #pragma unroll
         for (int o2 = 1; o2 < 64; o2 <<= 1) {
-            const long long y = __shfl_up(incl, o2);
+            const int y = __shfl_up(incl, o2);
             if (lane >= o2) incl += y;
         }
-        total = uniform64(__shfl(incl, 63));
+        total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
     } else {
-        total = total_bytes<D, HB>(p);
+        total = total_cost<D, HB>(p);
     }
     if (total == 0) return;
     const int G = used_workgroups(p, total);
     if (w >= G) return;
-    const long long lo = (long long)w * total / G;
-    const long long hi = (long long)(w + 1) * total / G;
+    const int lo = split_point(w, total, G);
+    const int hi = split_point(w + 1, total, G);
     int b;
     SeqUnits<D, HB> su;
     if (p.B <= 64) {
         const unsigned long long hit = __ballot(lane < p.B && incl > lo);
         b = __builtin_ctzll(hit);
-        off = uniform64(__shfl(incl - v, b));
+        off = __builtin_amdgcn_readfirstlane(__shfl(incl - v, b));
         su.init_counts(p, __builtin_amdgcn_readfirstlane(__shfl(cnt[0], b)),
                        __builtin_amdgcn_readfirstlane(__shfl(cnt[1], b)),
                        __builtin_amdgcn_readfirstlane(__shfl(cnt[2], b)));
@@ -885,14 +908,18 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
         if (b >= p.B) return;
         su.init(p, b);
     }
-    int h = (int)((lo - off) / su.bytes);
-    off += (long long)h * su.bytes;
+    int h = (int)((unsigned)(lo - off) / (unsigned)su.cost);
+    off += h * su.cost;
     float* plds = plds_all[threadIdx.x >> 6];
+    int tbase = 0;   // tickets taken by earlier pieces
     while (off < hi) {
         const int U0 = su.first_at_or_after(lo - off);
         const int U1 = su.first_at_or_after(hi - off);
-        if (U0 < U1) run_piece<D, HB>(p, su, b, h, U0, U1, b * p.Hkv + h + w, &ctr, plds, rec);
-        off += su.bytes;
+        if (U0 < U1) {
+            run_piece<D, HB>(p, su, b, h, U0, U1, tbase, b * p.Hkv + h + w, &ctr, plds, rec);
+            tbase += U1 - U0 + kAttnWaves;
+        }
+        off += su.cost;
         if (++h == p.Hkv) {
             h = 0;
             if (++b >= p.B) break;
@@ -922,14 +949,14 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
     const int tid = threadIdx.x, qd = tid % QPR, tgi = tid / QPR;
     if (tid < 64) {
         int w0 = 0, np = 0;
-        const long long total = total_bytes<D, HB>(p);
+        const int total = total_cost<D, HB>(p);
         if (total > 0) {
             SeqUnits<D, HB> su;
             su.init(p, b);
             if (su.units > 0) {
                 const int G = used_workgroups(p, total);
-                const long long first = seq_offset<D, HB>(p, b) + (long long)h * su.bytes;
-                const long long last = first + su.unit_start(su.units - 1);
+                const int first = seq_offset<D, HB>(p, b) + h * su.cost;
+                const int last = first + su.unit_start(su.units - 1);
                 w0 = owner_of(first, total, G);
                 np = owner_of(last, total, G) - w0 + 1;
             }

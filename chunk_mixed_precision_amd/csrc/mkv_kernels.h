@@ -57,7 +57,23 @@ struct QuantParams {
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnWaves = 8;             // wavefronts per attention workgroup (2 per SIMD)
-constexpr long long kAttnMinWgBytes = 128 << 10;  // smallest byte range given to one workgroup
+constexpr long long kAttnMinWgCost = 128 << 10;  // smallest cost range given to one workgroup
+// The split counts costs in granules of this many bytes, in 32-bit integers;
+// every unit's cost is a whole number of granules.
+constexpr int kAttnGranule = 512;
+// Largest whole-cache cost, in granules, that the split handles.
+constexpr long long kAttnMaxGranules = (1LL << 31) - 1;
+// Cost of a unit per byte, in sixteenths, for segment k (FP16, INT4, INT2)
+// and hb query heads per KV head: the workgroup time per byte measured on
+// each segment relative to INT4.  With one head per KV head the kernel
+// streams at the same rate on every segment; with grouped-query heads the
+// arithmetic per byte counts (an INT2 byte holds twice the codes of an INT4
+// byte, an FP16 byte needs no unpacking).  Equal-cost ranges finish together.
+constexpr int attn_cost16(int hb, int k) {
+    return hb == 1 ? 16
+         : hb == 2 ? (k == 0 ? 11 : k == 1 ? 16 : 22)
+                   : (k == 0 ? 7 : k == 1 ? 16 : 29);
+}
 // Query heads served by one row of lanes: with grouped-query attention a row
 // serves two heads of its KV head, so each code word is unpacked once for both.
 constexpr int attn_heads_per_row(int hb) { return hb == 1 ? 1 : 2; }

@@ -222,7 +222,9 @@ int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T,
  *   workspace   at least mkv_workspace_bytes(MKV_OP_ATTENTION, ...) bytes
  *               (tile partials; no initial contents needed).  Calls that
  *               overlap in time need separate workspaces.
- * Limits: d in {64, 128}; Hq/Hkv in {1, 2, 4}; 0 <= tail_len < 4096.
+ * Limits: d in {64, 128}; Hq/Hkv in {1, 2, 4}; 0 <= tail_len < 4096; the
+ * pools at capacity within 2^31 work-split granules of 512 bytes (weighted
+ * by bitwidth: 0.6 to 1 TiB of packed cache), else MKV_ERR_UNSUPPORTED.
  * A (b, h) with no cached token and tail_len == 0 yields zeros.
  * ---------------------------------------------------------------------- */
 int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq,
