@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--workload", default=configs.LLAMA2_7B_32K.name, choices=[w.name for w in configs.ALL])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle timing on the host (0 disables it)")
+    ap.add_argument("--routing-ablation", type=int, default=0, metavar="L",
+                    help="also time L-layer steps with routing sharing (one route, L x quantize + attend) "
+                         "and without it (every layer routes its own hidden states)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB (a known-size "
                          "kernel that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -128,6 +131,70 @@ def cpu_baseline(w, k, v, q, tab_bits, budget_s):
                    f"({t_attn:.1f} s); oracle quantize of the same slices {tokens / t_quant:.0f} tokens/s per "
                    f"head-slice ({t_quant:.1f} s); numpy, 1 thread"),
     }
+
+
+def routing_ablation(w, L, steps, warmup):
+    """Whole L-layer steps with and without routing sharing (MoQAE, Key
+    designs).  Every layer has its own K/V, query, hidden states and router;
+    with sharing, layer 0's tables serve every layer, without it each layer
+    routes its own chunks and gets its own tables and pool capacities."""
+    import numpy as np
+    import torch
+    from chunk_mixed_precision_amd import mkv, synth
+    dev = "cuda"
+    layers = []
+    for l in range(L):
+        x, w12, w3, b3 = synth.router_inputs(w, layer=l)
+        k, v = synth.kv(w, dev, layer=l)
+        layers.append({"x": x.to(dev), "w12": w12.to(dev), "w3": w3.to(dev), "b3": b3.to(dev),
+                       "k": k, "v": v, "q": synth.query(w, dev, layer=l),
+                       "tab": mkv.RouteTables(w.B, w.n, dev)})
+        del x
+    ws_route = torch.empty(mkv.workspace_bytes_route(w.B, w.T, w.D, w.I), dtype=torch.uint8, device=dev)
+    for ly in layers:
+        mkv.route_chunks(ly["tab"], w.C, x=ly["x"], w12=ly["w12"], w3=ly["w3"], b3=ly["b3"], workspace=ws_route)
+    torch.cuda.synchronize()
+
+    def caches_for(tabs):
+        out = []
+        for tab in tabs:
+            seg = tab.seg_count.cpu().numpy()
+            caps = [int(seg[:, kk].max()) for kk in range(3)]
+            c = mkv.PackedCache(w.B, w.Hkv, w.d, w.C, caps, tab.seg_count, dev)
+            out.append((c, mkv.attention_workspace(w.B, w.Hq, c, dev)))
+        return out
+
+    res = {"layers": L}
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    for mode in ("shared", "per_layer"):
+        tabs = [layers[0]["tab"]] * L if mode == "shared" else [ly["tab"] for ly in layers]
+        cw = caches_for(tabs)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+        def step(i, rec):
+            if rec:
+                ev[i][0].record()
+            for l, ly in enumerate(layers):
+                if mode == "per_layer" or l == 0:
+                    mkv.route_chunks(tabs[l], w.C, x=ly["x"], w12=ly["w12"], w3=ly["w3"], b3=ly["b3"],
+                                     workspace=ws_route)
+                mkv.quantize_pack_kv(ly["k"], ly["v"], tabs[l], cw[l][0])
+                mkv.mixed_kv_decode_attention(ly["q"], cw[l][0], out=out, workspace=cw[l][1])
+            if rec:
+                ev[i][1].record()
+
+        for i in range(warmup):
+            step(i, False)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            step(i, True)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev])
+        res[mode] = {"ms_per_step": round(float(t.mean()), 4),
+                     "chunk_mix_per_layer": [[int(s) for s in tb.seg_count.cpu().numpy().sum(0)] for tb in tabs]}
+        del cw
+    res["per_layer_over_shared"] = round(res["per_layer"]["ms_per_step"] / res["shared"]["ms_per_step"], 4)
+    return res
 
 
 def main():
@@ -262,6 +329,10 @@ def main():
                            "source": "profiles/pmc_traffic.json"}},
         },
     }
+    if args.routing_ablation > 0:
+        del caches, x
+        torch.cuda.empty_cache()
+        res["routing_ablation"] = routing_ablation(w, args.routing_ablation, max(3, args.steps // 4), 2)
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, k, v, q, tab.chunk_bits.cpu().numpy(), args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -28,32 +28,34 @@ def _gen(seed: int, stream: int, layer: int = 0, device="cpu") -> torch.Generato
 
 
 def router_inputs(w: Workload, tokens_per_seq: int = None, batch: int = None,
-                  chunk_offset: int = 0):
+                  chunk_offset: int = 0, layer: int = 0):
     """x [B, T, D] bf16 (chunk-structured), W12 [2I, D] bf16, W3 [3, I] f32,
     b3 [3] f32, all on the CPU.
 
     x_t = (a * mu_c + z_t) / sqrt(1 + a^2) with mu_c, z_t ~ N(0, I_D), where c
     is the chunk of token t (a = w.x_chunk_share; a = 0 gives iid N(0,1)).
     ``chunk_offset`` selects which chunks' hidden states to draw (appends
-    draw chunks after the prefill)."""
+    draw chunks after the prefill).  ``layer`` draws another block's hidden
+    states and router (every block has its own router; layer 0 is the block
+    whose routing is shared when routing sharing is on)."""
     B = w.B if batch is None else batch
     T = w.T if tokens_per_seq is None else tokens_per_seq
     D, I = w.D, w.I
     n = T // w.C
-    gz = _gen(w.seed, 1 + 1000 * chunk_offset)
+    gz = _gen(w.seed, 1 + 1000 * chunk_offset, layer)
     z = torch.randn((B, T, D), generator=gz, dtype=torch.float32)
     a = w.x_chunk_share
     if a > 0:
-        gm = _gen(w.seed, 9 + 1000 * chunk_offset)
+        gm = _gen(w.seed, 9 + 1000 * chunk_offset, layer)
         mu = torch.randn((B, n, 1, D), generator=gm, dtype=torch.float32)
         z = z.view(B, n, w.C, D)
         z.mul_(1.0 / math.sqrt(1 + a * a)).add_(mu, alpha=a / math.sqrt(1 + a * a))
         z = z.view(B, T, D)
     x = z.to(torch.bfloat16)
     del z
-    w12 = (torch.randn((2 * I, D), generator=_gen(w.seed, 2), dtype=torch.float32)
+    w12 = (torch.randn((2 * I, D), generator=_gen(w.seed, 2, layer), dtype=torch.float32)
            * w.router_std).to(torch.bfloat16)
-    w3 = torch.randn((3, I), generator=_gen(w.seed, 3), dtype=torch.float32) * w.router_std
+    w3 = torch.randn((3, I), generator=_gen(w.seed, 3, layer), dtype=torch.float32) * w.router_std
     b3 = torch.tensor(w.b3, dtype=torch.float32)
     return x, w12, w3, b3
 

@@ -148,6 +148,40 @@ def test_mixed_chunks_exhaustive(d, C, Hq, Hkv, B, T):
     full_check(w, tab, cache, out, k, v, q, w.n, tk, tv)
 
 
+def test_without_routing_sharing_per_layer_tables():
+    """The ablation without routing sharing (MoQAE, Key designs: RS off):
+    every block routes its own hidden states with its own router, so every
+    layer has its own tables, pools and capacities.  Each layer's route,
+    vote, reorder, quantize and attention stay at parity, and the layers'
+    tables differ (the ablation changes the routing)."""
+    w = configs.Workload(name="wo-rs", seed=91, B=2, Hq=4, Hkv=4, d=128, T=2048, C=128, D=256, I=128,
+                         layers=3, x_chunk_share=1.0, router_std=0.05, b3=(0.0, 0.02, 0.0))
+    note(f"without routing sharing {w.name}")
+    all_bits = []
+    for layer in range(w.layers):
+        x, w12, w3, b3 = synth.router_inputs(w, layer=layer)
+        tab = mkv.RouteTables(w.B, w.n, DEV)
+        logits = torch.empty((w.B, w.T, 3), dtype=torch.float32, device=DEV)
+        te = torch.empty((w.B, w.T), dtype=torch.uint8, device=DEV)
+        mkv.route_chunks(tab, w.C, x=x.to(DEV), w12=w12.to(DEV), w3=w3.to(DEV), b3=b3.to(DEV),
+                         logits=logits, token_expert=te)
+        torch.cuda.synchronize()
+        rep = P.check_router(x.view(-1, w.D), w12, w3, b3, w.I, P.to_np(logits).reshape(-1, 3),
+                             P.to_np(te).reshape(-1))
+        note(f"  layer {layer} router: {rep}")
+        assert rep["max_abs_logit_err"] < 1e-4
+        bits, rank, perm, seg = tables_np(tab)
+        P.check_vote_and_reorder(P.to_np(te), w.C, bits, rank, perm, seg)
+        note(f"  layer {layer} segment counts {seg.tolist()}")
+        k, v = synth.kv(w, DEV, layer=layer)
+        q = synth.query(w, DEV, layer=layer)
+        cache, out, _, _ = run_quant_attn(w, tab, k, v, q, w.n)
+        check_canary(cache, seg)
+        full_check(w, tab, cache, out, k, v, q, w.n)
+        all_bits.append(bits)
+    assert any(not np.array_equal(all_bits[0], b) for b in all_bits[1:])
+
+
 def test_constant_groups_and_signed_zeros():
     """Groups whose values are all equal (scale 0), -0/+0 extremes, and a
     group made of two values only."""
