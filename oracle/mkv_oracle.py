@@ -44,6 +44,16 @@ the design notes):
       a sign that depends on reduction order; s == 0 gives all-zero codes.
   R8  Attention is ordinary softmax attention over the dequantized cache
       (x_hat = code * s + mn), no mask, keys already position-encoded.
+  R9  Cocktail's chunk-level quantization search gives each chunk a bitwidth
+      from the similarity between the chunk and the query.  The page names no
+      measure, summary or rule.  Plainest reading: the chunk is summarised by
+      the mean of its tokens' embeddings, the similarity is the cosine
+      between that mean and the query embedding (a zero vector gives 0), and
+      two thresholds split the range: sim >= tau_hi -> FP16,
+      tau_lo <= sim < tau_hi -> INT4, sim < tau_lo -> INT2 (more similar
+      chunks matter more to the query and keep more bits).  Routing freezing
+      may pin chunk 0 as for the router.  parity unpinned against the
+      authors' search (no code or constants exist).
 """
 from __future__ import annotations
 
@@ -258,6 +268,59 @@ def attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray) -> np.ndarray
 # whole-path helpers (still step by step; used by tests and the bench's
 # CPU-baseline leg)
 # --------------------------------------------------------------------------
+# --------------------------------------------------------------------------
+# similarity-based chunk selection  [Cocktail abstract: chunk-level
+# quantization search; reading R9]
+# --------------------------------------------------------------------------
+def chunk_similarity(x: np.ndarray, qe: np.ndarray, chunk: int) -> np.ndarray:
+    """Cosine similarity between each chunk's mean token embedding and the
+    query embedding, float64.
+
+    x  [B, T, D] embeddings (float64 values), T a multiple of ``chunk``
+    qe [B, D] query embeddings
+    Returns sim [B, T/chunk]; 0 where either vector is zero.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    qe = np.asarray(qe, dtype=np.float64)
+    B, T, D = x.shape
+    n = T // chunk
+    sim = np.zeros((B, n))
+    for b in range(B):
+        qn = np.sqrt(np.dot(qe[b], qe[b]))
+        for c in range(n):
+            mean = x[b, c * chunk:(c + 1) * chunk].sum(axis=0) / chunk
+            mn = np.sqrt(np.dot(mean, mean))
+            if mn > 0 and qn > 0:
+                sim[b, c] = np.dot(mean, qe[b]) / (mn * qn)
+    return sim
+
+
+def similarity_experts(sim: np.ndarray, tau_hi: float, tau_lo: float,
+                       freeze_first: bool = False, chunk_offset: int = 0) -> np.ndarray:
+    """Expert index of each chunk from its similarity (reading R9): FP16 at
+    or above tau_hi, INT4 at or above tau_lo, INT2 below.  With freezing,
+    the sequence's chunk 0 (global index 0, i.e. only when chunk_offset is
+    0) is FP16."""
+    sim = np.asarray(sim, dtype=np.float64)
+    e = np.where(sim >= tau_hi, 0, np.where(sim >= tau_lo, 1, 2)).astype(np.int64)
+    if freeze_first and chunk_offset == 0 and e.shape[1] > 0:
+        e[:, 0] = 0
+    return e
+
+
+def select_by_similarity(x_bits: np.ndarray, qe_bits: np.ndarray, chunk: int, tau_hi: float,
+                         tau_lo: float, freeze_first: bool = False):
+    """x_bits [B, T, D] and qe_bits [B, D] bf16 bit patterns.  Returns
+    (sim [B, n] f64, chunk expert [B, n], perm, rank, seg_count)."""
+    B, T, D = x_bits.shape
+    x = bf16_bits_to_f64(x_bits.reshape(B * T, D)).reshape(B, T, D)
+    qe = bf16_bits_to_f64(qe_bits)
+    sim = chunk_similarity(x, qe, chunk)
+    e = similarity_experts(sim, tau_hi, tau_lo, freeze_first)
+    perm, rank, seg = reorder(e)
+    return sim, e, perm, rank, seg
+
+
 def route(x_bits: np.ndarray, w12_bits: np.ndarray, w3: np.ndarray,
           b3: np.ndarray, inner: int, chunk: int, freeze_first: bool = True):
     """x_bits [B, T, D] bf16 bit patterns.  Returns (logits [B,T,3] f64,

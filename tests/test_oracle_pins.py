@@ -420,3 +420,91 @@ def test_pins_catch_vote_tie_mistake():
     assert ok == [0, 1]
     wrong = [max(set(r.tolist()), key=lambda k: (r.tolist().count(k), k)) for r in labs]
     assert wrong != ok
+
+
+# ---------------------------------------------------------------- similarity selection (Cocktail)
+def _sim_cases():
+    with open(os.path.join(GOLD, "similarity_hand_cases.json")) as f:
+        return json.load(f)
+
+
+def check_similarity_on_cases(sim_fn, experts_fn):
+    """Hand-worked chunks (Cocktail abstract, chunk-level quantization
+    search; tests/golden/similarity_hand_cases.json)."""
+    case = _sim_cases()
+    C = case["chunk"]
+    for seq in case["sequences"]:
+        x = np.array([tok for ch in seq["chunks"] for tok in ch["tokens"]], dtype=np.float64)[None]
+        qe = np.array(seq["query"], dtype=np.float64)[None]
+        sim = sim_fn(x, qe, C)[0]
+        e = experts_fn(sim[None], case["tau_hi"], case["tau_lo"])[0]
+        for i, ch in enumerate(seq["chunks"]):
+            assert abs(sim[i] - ch["sim"]) <= 1e-12, (ch["note"], sim[i])
+            assert e[i] == ch["expert"], ch["note"]
+
+
+def test_similarity_hand_cases():
+    check_similarity_on_cases(orc.chunk_similarity, orc.similarity_experts)
+
+
+def test_similarity_closed_forms_and_invariances():
+    rng = np.random.default_rng(7)
+    B, C, D, n = 2, 16, 64, 6
+    x = rng.standard_normal((B, n * C, D))
+    qe = rng.standard_normal((B, D))
+    sim = orc.chunk_similarity(x, qe, C)
+    assert np.all(np.abs(sim) <= 1 + 1e-12)
+    # positive scaling of a chunk's tokens or of the query, and the token
+    # order inside a chunk, change nothing
+    x2 = x.copy()
+    x2[:, :C] *= 3.5
+    x2[:, C:2 * C] = x2[:, C:2 * C][:, ::-1]
+    assert np.allclose(orc.chunk_similarity(x2, qe * 0.25, C), sim, atol=1e-12)
+    # a chunk of copies of the query has similarity 1, of its negation -1;
+    # a chunk orthogonal to the query has 0
+    x3 = x.copy()
+    x3[:, :C] = qe[:, None, :]
+    x3[:, C:2 * C] = -2.0 * qe[:, None, :]
+    ortho = np.zeros_like(qe)
+    ortho[:, 0], ortho[:, 1] = qe[:, 1], -qe[:, 0]
+    x3[:, 2 * C:3 * C] = ortho[:, None, :]
+    s3 = orc.chunk_similarity(x3, qe, C)
+    assert np.allclose(s3[:, 0], 1.0) and np.allclose(s3[:, 1], -1.0) and np.allclose(s3[:, 2], 0.0, atol=1e-12)
+
+
+def test_similarity_experts_thresholds_and_freezing():
+    sim = np.array([[0.2, 0.95, 0.5, -0.1, 0.9, 0.0]])
+    assert orc.similarity_experts(sim, 0.9, 0.0).tolist() == [[1, 0, 1, 2, 0, 1]]
+    assert orc.similarity_experts(sim, 0.9, 0.0, freeze_first=True).tolist() == [[0, 0, 1, 2, 0, 1]]
+    # appended chunks never include the sequence's chunk 0
+    assert orc.similarity_experts(sim, 0.9, 0.0, freeze_first=True, chunk_offset=3).tolist() == [[1, 0, 1, 2, 0, 1]]
+
+
+def _sim_mean_of_cosines(x, qe, C):
+    B, T, D = x.shape
+    out = np.zeros((B, T // C))
+    for b in range(B):
+        for c in range(T // C):
+            cs = []
+            for t in range(c * C, (c + 1) * C):
+                nx, nq = np.linalg.norm(x[b, t]), np.linalg.norm(qe[b])
+                cs.append(0.0 if nx == 0 or nq == 0 else float(np.dot(x[b, t], qe[b]) / (nx * nq)))
+            out[b, c] = np.mean(cs)
+    return out
+
+
+def _experts_strict(sim, hi, lo):
+    return np.where(sim > hi, 0, np.where(sim > lo, 1, 2))
+
+
+def _experts_swapped(sim, hi, lo):
+    return np.where(sim >= hi, 2, np.where(sim >= lo, 1, 0))
+
+
+@pytest.mark.parametrize("variant", ["mean_of_cosines", "strict_thresholds", "swapped_experts"])
+def test_pins_catch_planted_similarity_mistakes(variant):
+    sim_fn = _sim_mean_of_cosines if variant == "mean_of_cosines" else orc.chunk_similarity
+    ex_fn = {"strict_thresholds": _experts_strict, "swapped_experts": _experts_swapped}.get(variant,
+                                                                                          orc.similarity_experts)
+    with pytest.raises(AssertionError):
+        check_similarity_on_cases(sim_fn, ex_fn)
