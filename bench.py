@@ -20,7 +20,10 @@ not while attention reads.
 
 Prints one JSON line.  value = decode-attention effective GB/s (packed KV
 bytes + q + out per launch / attention time); the quantize rate, router rate
-and per-kernel times are reported beside it.
+and per-kernel times are reported beside it, and so is the time of the
+alternative selector (mkv_select_chunks_by_similarity: chunk bitwidths from
+the similarity to a query embedding) over the same hidden states, timed on
+its own after the steps.
 """
 from __future__ import annotations
 
@@ -271,6 +274,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the alternative selector (similarity to a query embedding) on the same hidden states
+    qe = synth.query_embedding(w).to(dev)
+    tab_sim = mkv.RouteTables(w.B, w.n, dev)
+    ws_sim = torch.empty(mkv.workspace_bytes_similarity(w.B, w.T, w.D, w.C), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        mkv.select_chunks_by_similarity(tab_sim, w.C, x, qe, 0.3, 0.0, workspace=ws_sim)
+    ev_sim = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
+    for i in range(nev):
+        ev_sim[i][0].record()
+        mkv.select_chunks_by_similarity(tab_sim, w.C, x, qe, 0.3, 0.0, workspace=ws_sim)
+        ev_sim[i][1].record()
+    torch.cuda.synchronize()
+    t_sim = np.array([a.elapsed_time(b) for a, b in ev_sim]) * 1e-3
+    sim_bytes = w.B * w.T * w.D * 2 + w.B * w.D * 2 + w.B * w.n * (1 + 4 + 4)
+
     t_pack = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
     t_route = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
     t_attn = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(nev)]) * 1e-3
@@ -319,6 +337,12 @@ def main():
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round((pack_read + pack_write) / float(t_pack.mean()) / 1e9 / HBM_PEAK_GBS, 4),
                                   "bytes_per_launch": pack_read + pack_write}},
+            "select_similarity": {
+                "us": round(float(t_sim.mean()) * 1e6, 2),
+                "roofline": {"bound": "hbm", "achieved": round(sim_bytes / float(t_sim.mean()) / 1e9, 2),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(sim_bytes / float(t_sim.mean()) / 1e9 / HBM_PEAK_GBS, 4),
+                             "bytes_per_launch": sim_bytes}},
             "attend": {"us": round(a_mean * 1e6, 2), "us_p10": round(float(np.percentile(t_attn, 10)) * 1e6, 2),
                        "us_p90": round(float(np.percentile(t_attn, 90)) * 1e6, 2), "bytes": attn_bytes,
                        "traffic": None if traffic is None else {

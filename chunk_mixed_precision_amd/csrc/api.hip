@@ -93,6 +93,12 @@ size_t mkv_workspace_bytes(int op, int a, int b, int c, int e, int f, const int*
         if (B <= 0 || T <= 0 || I <= 0 || I % mkv::kRouterBI) return 0;
         return (size_t)(I / mkv::kRouterBI) * B * T * 3 * sizeof(float);
     }
+    if (op == MKV_OP_SIMILARITY) {
+        const int B = a, T = b, D = c, C = e;
+        if (B <= 0 || T <= 0 || D <= 0 || C <= 0 || T % C) return 0;
+        const size_t ds = ((size_t)D + mkv::kSimSlice - 1) / mkv::kSimSlice;
+        return (size_t)B * (T / C) * ds * 16;
+    }
     if (op == MKV_OP_ATTENTION) {
         const int B = a, Hq = b, Hkv = c, d = e, C = f;
         if (!caps || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (d != 64 && d != 128) || C <= 0 || C % 32) return 0;
@@ -147,6 +153,42 @@ int mkv_route_chunks(const void* x_bf16, const void* w12_bf16, const float* w3, 
     vp.B = B; vp.T = T; vp.C = C; vp.n_max = tab->n_max; vp.chunk_offset = chunk_offset;
     vp.freeze_first = (flags & MKV_FREEZE_FIRST) ? 1 : 0;
     int s = hip_status(mkv::launch_vote(vp, n_new, st));
+    if (s) return s;
+    mkv::ReorderParams op{tab->chunk_bits, tab->chunk_rank, tab->perm, tab->seg_count,
+                          chunk_offset + n_new, tab->n_max, nullptr};
+    return hip_status(mkv::launch_reorder(op, B, st));
+}
+
+int mkv_select_chunks_by_similarity(const void* x_bf16, const void* qe_bf16, int B, int T, int D, int C,
+                                    float tau_hi, float tau_lo, unsigned flags, float* sim,
+                                    const mkv_tables* tab, int chunk_offset, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    const bool append = (flags & MKV_APPEND) != 0;
+    if (flags & ~(MKV_FREEZE_FIRST | MKV_APPEND)) return MKV_ERR_ARG;
+    if (!tab || !tab->chunk_bits || !tab->chunk_rank || !tab->perm || !tab->seg_count) return MKV_ERR_ARG;
+    if (!x_bf16 || !qe_bf16 || !aligned16(x_bf16) || !aligned16(qe_bf16)) return MKV_ERR_ARG;
+    if (sim && !aligned16(sim)) return MKV_ERR_ARG;
+    if (B <= 0 || T <= 0 || C <= 0 || D <= 0) return MKV_ERR_ARG;
+    if (!(tau_lo <= tau_hi)) return MKV_ERR_ARG;   // also rejects NaN thresholds
+    if (C % 32 != 0 || C > 1024 || T % C != 0 || D % 64 != 0) return MKV_ERR_UNSUPPORTED;
+    if (chunk_offset < 0 || (!append && chunk_offset != 0)) return MKV_ERR_ARG;
+    const int n_new = T / C;
+    if (tab->n_max <= 0 || chunk_offset + n_new > tab->n_max) return MKV_ERR_ARG;
+    if (B > 65535 || n_new > 65535) return MKV_ERR_UNSUPPORTED;
+    const size_t need = mkv_workspace_bytes(MKV_OP_SIMILARITY, B, T, D, C, 0, nullptr);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return MKV_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    mkv::SimParams sp{};
+    sp.x = static_cast<const uint16_t*>(x_bf16);
+    sp.qe = static_cast<const uint16_t*>(qe_bf16);
+    sp.part = static_cast<float4*>(workspace);
+    sp.sim = sim;
+    sp.chunk_bits = tab->chunk_bits;
+    sp.B = B; sp.T = T; sp.D = D; sp.C = C; sp.n_max = tab->n_max; sp.chunk_offset = chunk_offset;
+    sp.ds = (D + mkv::kSimSlice - 1) / mkv::kSimSlice;
+    sp.tau_hi = tau_hi; sp.tau_lo = tau_lo;
+    sp.freeze_first = (flags & MKV_FREEZE_FIRST) ? 1 : 0;
+    int s = hip_status(mkv::launch_similarity(sp, st));
     if (s) return s;
     mkv::ReorderParams op{tab->chunk_bits, tab->chunk_rank, tab->perm, tab->seg_count,
                           chunk_offset + n_new, tab->n_max, nullptr};

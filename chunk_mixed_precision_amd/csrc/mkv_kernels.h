@@ -43,6 +43,20 @@ struct ReorderParams {
     int32_t* bad;           // optional: set when a chunk's bitwidth is invalid
 };
 
+// ---------------------------------------------------------------- similarity selection
+constexpr int kSimSlice = 512;          // embedding dims per partial-sum workgroup (64 lanes x 8)
+
+struct SimParams {
+    const uint16_t* x;      // [B][T][D] bf16 embeddings of the new chunks' tokens
+    const uint16_t* qe;     // [B][D] bf16 query embeddings
+    float4* part;           // [B][n_new][ds]: (q.S, |S|^2, |q|^2, 0) per dim slice
+    float* sim;             // [B][n_new] out, optional
+    uint8_t* chunk_bits;    // [B][n_max]
+    int B, T, D, C, n_max, chunk_offset, ds;
+    float tau_hi, tau_lo;
+    int freeze_first;
+};
+
 // ---------------------------------------------------------------- quantize
 struct QuantParams {
     const uint16_t* k;      // [B][Hkv][T][d] fp16 bits
@@ -98,6 +112,7 @@ hipError_t launch_router(const RouterParams& rp, hipStream_t st);
 hipError_t launch_vote(const VoteParams& vp, int n_new, hipStream_t st);
 hipError_t launch_reorder(const ReorderParams& rp, int B, hipStream_t st);
 hipError_t launch_quant(const QuantParams& qp, int D, int ngroups, hipStream_t st);
+hipError_t launch_similarity(const SimParams& sp, hipStream_t st);
 hipError_t launch_attention(const AttnParams& ap, int D, int HB, hipStream_t st);
 
 }  // namespace mkv

@@ -31,9 +31,11 @@ MKV_APPEND = 0x4
 
 MKV_OP_ROUTE = 1
 MKV_OP_ATTENTION = 2
+MKV_OP_SIMILARITY = 3
 
 EXPORTED = (
-    "mkv_route_chunks", "mkv_quantize_pack_kv", "mkv_mixed_kv_decode_attention",
+    "mkv_route_chunks", "mkv_select_chunks_by_similarity", "mkv_quantize_pack_kv",
+    "mkv_mixed_kv_decode_attention",
     "mkv_workspace_bytes", "mkv_group_bytes", "mkv_pool_bytes",
     "mkv_status_string", "mkv_last_hip_error", "mkv_version",
 )
@@ -72,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.mkv_route_chunks.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, u, vp,
                                        ctypes.POINTER(MkvTables), i, vp, sz, vp]
         L.mkv_route_chunks.restype = i
+        L.mkv_select_chunks_by_similarity.argtypes = [vp, vp, i, i, i, i, ctypes.c_float, ctypes.c_float, u,
+                                                      vp, ctypes.POINTER(MkvTables), i, vp, sz, vp]
+        L.mkv_select_chunks_by_similarity.restype = i
         L.mkv_quantize_pack_kv.argtypes = [vp, vp, i, i, ctypes.POINTER(MkvTables),
                                            ctypes.POINTER(MkvCache), vp]
         L.mkv_quantize_pack_kv.restype = i
@@ -121,6 +126,10 @@ def pool_bytes(bits: int, B: int, Hkv: int, cap: int, d: int, C: int) -> int:
 
 def workspace_bytes_route(B: int, T: int, D: int, I: int) -> int:
     return int(lib().mkv_workspace_bytes(MKV_OP_ROUTE, B, T, D, I, 0, None))
+
+
+def workspace_bytes_similarity(B: int, T: int, D: int, C: int) -> int:
+    return int(lib().mkv_workspace_bytes(MKV_OP_SIMILARITY, B, T, D, C, 0, None))
 
 
 def workspace_bytes_attention(B: int, Hq: int, Hkv: int, d: int, C: int, caps: Sequence[int]) -> int:
@@ -197,6 +206,24 @@ def route_chunks(tables: RouteTables, C: int, *, x: torch.Tensor = None, w12: to
                                 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                 _stream(stream))
     _check(st, "mkv_route_chunks")
+
+
+def select_chunks_by_similarity(tables: RouteTables, C: int, x: torch.Tensor, qe: torch.Tensor,
+                                tau_hi: float, tau_lo: float, *, sim: torch.Tensor = None,
+                                freeze_first: bool = True, chunk_offset: int = 0, append: bool = False,
+                                workspace: torch.Tensor = None, stream=None):
+    """mkv_select_chunks_by_similarity: x [B,T,D] bf16 token embeddings, qe
+    [B,D] bf16 query embeddings; sim (optional) receives [B, T/C] f32."""
+    flags = (MKV_FREEZE_FIRST if freeze_first else 0) | (MKV_APPEND if append else 0)
+    B, T, D = x.shape
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes_similarity(B, T, D, C), dtype=torch.uint8, device=x.device)
+    tab = tables.c()
+    st = lib().mkv_select_chunks_by_similarity(_ptr(x), _ptr(qe), B, T, D, C, float(tau_hi), float(tau_lo),
+                                               flags, _ptr(sim), ctypes.byref(tab), chunk_offset,
+                                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                               _stream(stream))
+    _check(st, "mkv_select_chunks_by_similarity")
 
 
 def quantize_pack_kv(k: torch.Tensor, v: torch.Tensor, tables: RouteTables, cache: PackedCache,

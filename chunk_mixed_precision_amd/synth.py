@@ -60,6 +60,21 @@ def router_inputs(w: Workload, tokens_per_seq: int = None, batch: int = None,
     return x, w12, w3, b3
 
 
+def query_embedding(w: Workload, batch: int = None, layer: int = 0) -> torch.Tensor:
+    """qe [B, D] bf16 on the CPU: a query embedding drawn near the chunk mean
+    mu_c of one seeded chunk c of each sequence (the mu_c of router_inputs),
+    qe = (mu_c + z) / sqrt(2), z ~ N(0, I_D); with iid hidden states
+    (x_chunk_share = 0) just z."""
+    B = w.B if batch is None else batch
+    D, n = w.D, w.T // w.C
+    z = torch.randn((B, D), generator=_gen(w.seed, 11, layer), dtype=torch.float32)
+    if w.x_chunk_share > 0:
+        mu = torch.randn((B, n, 1, D), generator=_gen(w.seed, 9, layer), dtype=torch.float32)
+        pick = torch.randint(0, n, (B,), generator=_gen(w.seed, 10, layer))
+        z = (mu[torch.arange(B), pick, 0] + z) / math.sqrt(2.0)
+    return z.to(torch.bfloat16)
+
+
 def outlier_mask(w: Workload) -> torch.Tensor:
     """[Hkv, d] float multiplier for the key columns (KIVI-style outlier
     channels): channels 0..k-1 of every head, or a seeded set of columns."""

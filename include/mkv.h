@@ -68,8 +68,9 @@ extern "C" {
                                  kept and the reorder covers them too      */
 
 /* ---- workspace query ops ------------------------------------------------ */
-#define MKV_OP_ROUTE     1
-#define MKV_OP_ATTENTION 2
+#define MKV_OP_ROUTE      1
+#define MKV_OP_ATTENTION  2
+#define MKV_OP_SIMILARITY 3
 
 /* Routing tables of a batch of sequences (routing sharing: one table serves
  * every layer and head).  All arrays are device memory, row stride n_max:
@@ -178,6 +179,35 @@ int mkv_route_chunks(const void* x_bf16, const void* w12_bf16,
                      size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * 1b. mkv_select_chunks_by_similarity — bitwidths from query-chunk
+ *    similarity instead of the router (Cocktail abstract: chunk-level
+ *    quantization search), then the same reorder tables as call 1.
+ *
+ *   x_bf16     [B][T][D] bf16 embeddings of the T = n_new*C tokens of chunks
+ *              chunk_offset .. chunk_offset+n_new-1 of each sequence
+ *   qe_bf16    [B][D] bf16 query embedding of each sequence
+ *   tau_hi, tau_lo  thresholds, tau_lo <= tau_hi
+ *   sim        [B][n_new] fp32 out (optional, may be NULL): each new
+ *              chunk's similarity
+ *   flags      MKV_FREEZE_FIRST (chunk 0 of each sequence FP16) | MKV_APPEND
+ *   tab, chunk_offset   as in call 1 (chunk_offset must be 0 without
+ *              MKV_APPEND)
+ *   workspace  at least mkv_workspace_bytes(MKV_OP_SIMILARITY, ...) bytes
+ * A chunk's similarity is the cosine between the sum (the direction of the
+ * mean) of its tokens' embeddings and the query embedding, in fp32, or 0
+ * when either vector is zero.  Its bitwidth is 16 when sim >= tau_hi, 4
+ * when tau_lo <= sim < tau_hi, 2 otherwise.  The reorder then covers chunks
+ * [0, chunk_offset + n_new) exactly as in call 1.
+ * Limits: D % 64 == 0; C % 32 == 0, C <= 1024; B, n_new <= 65535.
+ * ---------------------------------------------------------------------- */
+int mkv_select_chunks_by_similarity(const void* x_bf16, const void* qe_bf16,
+                                    int B, int T, int D, int C,
+                                    float tau_hi, float tau_lo, unsigned flags,
+                                    float* sim, const mkv_tables* tab,
+                                    int chunk_offset, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * 2. mkv_quantize_pack_kv — quantize and pack the K/V of routed chunks.
  *    MoQAE "Overall framework" (cache quantized at the voted bitwidth) and
  *    "Related work" (keys per channel); Cocktail abstract (chunks written to
@@ -239,6 +269,7 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq,
  *   MKV_OP_ROUTE:     a = B, b = T, c = D, e = I (f, g unused)
  *   MKV_OP_ATTENTION: a = B, b = Hq, c = Hkv, e = d, f = C, and `cache_caps`
  *                     points to the cache's cap[3] (host memory)
+ *   MKV_OP_SIMILARITY: a = B, b = T, c = D, e = C (f, cache_caps unused)
  * Returns 0 for an unknown op or invalid sizes.                          */
 size_t mkv_workspace_bytes(int op, int a, int b, int c, int e, int f,
                            const int* cache_caps);

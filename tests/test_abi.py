@@ -144,3 +144,33 @@ def test_attention_argument_errors():
     assert attn(tail_len=4096, tk=0x800, tv=0x900) == E.MKV_ERR_ARG
     assert attn() == E.MKV_ERR_WORKSPACE
     assert attn(ws=0x9000, wsb=64) == E.MKV_ERR_WORKSPACE
+
+
+def select(**kw):
+    a = dict(x=0x100, qe=0x200, B=1, T=256, D=256, C=128, hi=0.5, lo=0.0, flags=mkv.MKV_FREEZE_FIRST, sim=None,
+             tab=_tables(), off=0, ws=None, wsb=0)
+    a.update(kw)
+    tab = a["tab"]
+    return mkv.lib().mkv_select_chunks_by_similarity(a["x"], a["qe"], a["B"], a["T"], a["D"], a["C"], a["hi"],
+                                                     a["lo"], a["flags"], a["sim"],
+                                                     None if tab is None else ctypes.byref(tab), a["off"],
+                                                     a["ws"], a["wsb"], None)
+
+
+def test_similarity_selection_argument_errors():
+    E = mkv
+    assert select(tab=None) == E.MKV_ERR_ARG
+    assert select(x=None) == E.MKV_ERR_ARG
+    assert select(qe=0x204) == E.MKV_ERR_ARG                     # misaligned
+    assert select(sim=0x304) == E.MKV_ERR_ARG
+    assert select(hi=0.0, lo=0.5) == E.MKV_ERR_ARG               # tau_lo > tau_hi
+    assert select(hi=float("nan")) == E.MKV_ERR_ARG
+    assert select(C=48) == E.MKV_ERR_UNSUPPORTED
+    assert select(T=200) == E.MKV_ERR_UNSUPPORTED
+    assert select(D=100) == E.MKV_ERR_UNSUPPORTED
+    assert select(off=1) == E.MKV_ERR_ARG                        # offset without MKV_APPEND
+    assert select(tab=_tables(n_max=1)) == E.MKV_ERR_ARG         # 2 chunks > n_max
+    assert select(flags=mkv.MKV_LOGITS_IN) == E.MKV_ERR_ARG      # not a flag of this call
+    assert select() == E.MKV_ERR_WORKSPACE                       # no workspace
+    assert select(ws=0x9000, wsb=16) == E.MKV_ERR_WORKSPACE      # too small
+    assert mkv.workspace_bytes_similarity(2, 1024, 4096, 256) == 2 * 4 * 8 * 16
