@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--routing-ablation", type=int, default=0, metavar="L",
                     help="also time L-layer steps with routing sharing (one route, L x quantize + attend) "
                          "and without it (every layer routes its own hidden states)")
+    ap.add_argument("--decode-steps", type=int, default=0, metavar="N",
+                    help="also time N streaming-decode steps (one token per sequence, full chunks routed, "
+                         "quantized and appended) on the grouped-query workload")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB (a known-size "
                          "kernel that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -198,6 +201,47 @@ def routing_ablation(w, L, steps, warmup):
         del cw
     res["per_layer_over_shared"] = round(res["per_layer"]["ms_per_step"] / res["shared"]["ms_per_step"], 4)
     return res
+
+
+def streaming_decode(steps: int):
+    """Streaming decode on the llama3-8b GQA shape: the 8192-token prefill
+    (drawn chunk mix) in the packed cache, then `steps` steps of one token
+    per sequence into the fp16 tail; every C-th step routes, quantizes and
+    appends the completed chunk (the router on the chunk's hidden states)."""
+    import numpy as np
+    import torch
+    from chunk_mixed_precision_amd import configs, decode, synth
+    dev = "cuda"
+    w = configs.BY_NAME["llama3-8b-gqa-B64-T8192+256-C256"]
+    _, w12, w3, b3 = synth.router_inputs(w, tokens_per_seq=w.C, batch=1)
+    k, v = synth.kv(w, dev)
+    logits = synth.one_hot_logits(synth.drawn_chunk_experts(w), w.C).to(dev)
+    n_max = w.n + (steps + w.C - 1) // w.C + 1
+    sess = decode.DecodeSession(w.B, w.Hq, w.Hkv, w.d, w.C, 1, w12.to(dev), w3.to(dev), b3.to(dev),
+                                max_chunks=n_max)
+    sess.prefill(None, [(k, v)], logits=logits)
+    del k, v, logits
+    xs, ks, vs, qs = synth.decode_tokens(w, steps, dev)
+    out = [torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)]
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    flush = []
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        sess.step(xs[s], [(ks[s], vs[s])], [qs[s]], out=out)
+        ev[s][1].record()
+        flush.append(sess.tail_len == 0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    fl = np.array(flush)
+    return {"workload": w.name, "layers": 1, "steps": steps, "prefill_tokens": w.T,
+            "context_tokens_at_end": w.T + steps,
+            "step_us": round(float(t[~fl].mean()), 2), "step_us_p90": round(float(np.percentile(t[~fl], 90)), 2),
+            "flush_step_us": None if not fl.any() else round(float(t[fl].mean()), 2),
+            "flushes": int(fl.sum()), "pool_relayouts": sess.grown,
+            "decode_tokens_per_s": round(w.B * steps / wall, 1)}
 
 
 def main():
@@ -357,6 +401,8 @@ def main():
         del caches, x
         torch.cuda.empty_cache()
         res["routing_ablation"] = routing_ablation(w, args.routing_ablation, max(3, args.steps // 4), 2)
+    if args.decode_steps > 0:
+        res["streaming_decode"] = streaming_decode(args.decode_steps)
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, k, v, q, tab.chunk_bits.cpu().numpy(), args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -220,7 +220,7 @@ int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T, int chun
 }
 
 int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq, const mkv_cache* cache,
-                                  const void* tail_k_fp16, const void* tail_v_fp16, int tail_len,
+                                  const void* tail_k_fp16, const void* tail_v_fp16, int tail_len, int tail_stride,
                                   float* out, void* workspace, size_t workspace_bytes, void* stream) {
     if (!q_fp16 || !out || !aligned16(q_fp16) || !aligned16(out)) return MKV_ERR_ARG;
     if (!valid_cache(cache)) return MKV_ERR_ARG;
@@ -232,6 +232,8 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq, const mkv_cache* c
     if ((long)cache->B * Hq > 2147483647L) return MKV_ERR_UNSUPPORTED;
     if (tail_len < 0 || tail_len >= 4096) return MKV_ERR_ARG;
     if (tail_len > 0 && (!tail_k_fp16 || !tail_v_fp16)) return MKV_ERR_ARG;
+    if (tail_stride == 0) tail_stride = tail_len;
+    if (tail_stride < tail_len) return MKV_ERR_ARG;
     {   // the work split counts the cost of the whole cache at capacity in 32-bit granules
         const int gpi = (512 / cache->d) * mkv::attn_heads_per_row(g) / g;   // group blocks per unit
         const int bits[3] = {16, 4, 2};
@@ -259,9 +261,41 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq, const mkv_cache* c
     ap.tail_k = static_cast<const uint16_t*>(tail_k_fp16);
     ap.tail_v = static_cast<const uint16_t*>(tail_v_fp16);
     ap.tail_len = tail_len;
+    ap.tail_stride = tail_stride;
     ap.out = out;
     ap.qscale = (float)(1.4426950408889634 / sqrt((double)cache->d));
     return hip_status(mkv::launch_attention(ap, cache->d, g, (hipStream_t)stream));
+}
+
+int mkv_append_tail_rows(const void* a_new, const void* b_new, void* a_tail, void* b_tail, int rows, int width,
+                         int tail_stride, int pos, void* stream) {
+    if (!a_new || !a_tail || (b_new == nullptr) != (b_tail == nullptr)) return MKV_ERR_ARG;
+    if (!aligned16(a_new) || !aligned16(a_tail) || (b_new && (!aligned16(b_new) || !aligned16(b_tail))))
+        return MKV_ERR_ARG;
+    if (rows <= 0 || width <= 0 || tail_stride <= 0 || pos < 0 || pos >= tail_stride) return MKV_ERR_ARG;
+    if (width % 8) return MKV_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t rb = (size_t)width * 2, pitch = (size_t)tail_stride * rb;
+    int s = hip_status(mkv::launch_copy_rows(a_new, rb, static_cast<char*>(a_tail) + (size_t)pos * rb, pitch, rb,
+                                             rows, st));
+    if (s || !b_new) return s;
+    return hip_status(mkv::launch_copy_rows(b_new, rb, static_cast<char*>(b_tail) + (size_t)pos * rb, pitch, rb,
+                                            rows, st));
+}
+
+int mkv_grow_pool(const void* src, void* dst, int bits, int B, int Hkv, int cap_old, int cap_new, int d, int C,
+                  void* stream) {
+    if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MKV_ERR_ARG;
+    if (B <= 0 || Hkv <= 0 || cap_old < 0 || cap_new < cap_old || C <= 0 || C % mkv::kGroup) return MKV_ERR_ARG;
+    const size_t slot = mkv_pool_bytes(bits, 1, 1, 1, d, C);
+    if (!slot) return MKV_ERR_UNSUPPORTED;
+    if ((long long)B * Hkv > 2147483647LL) return MKV_ERR_UNSUPPORTED;
+    const char* s8 = static_cast<const char*>(src);
+    char* d8 = static_cast<char*>(dst);
+    const size_t old_bytes = (size_t)B * Hkv * cap_old * slot, new_bytes = (size_t)B * Hkv * cap_new * slot;
+    if (s8 < d8 + new_bytes && d8 < s8 + old_bytes) return MKV_ERR_ARG;   // overlap
+    return hip_status(mkv::launch_copy_rows(src, (size_t)cap_old * slot, dst, (size_t)cap_new * slot,
+                                            (size_t)cap_old * slot, B * Hkv, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -975,7 +975,7 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
         const int hq = h * HB + hb;
         if (p.tail_len > 0) {
             const uint16_t* qp = p.q + ((size_t)b * p.Hq + hq) * D;
-            const uint16_t* tk = p.tail_k + (size_t)bh * p.tail_len * D;
+            const uint16_t* tk = p.tail_k + (size_t)bh * p.tail_stride * D;
             for (int t = tid; t < p.tail_len; t += NT) {
                 float s = 0.f;
                 for (int c = 0; c < D; ++c)
@@ -1006,7 +1006,7 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
             }
         }
         if (p.tail_len > 0) {
-            const uint16_t* tv = p.tail_v + (size_t)bh * p.tail_len * D + 4 * qd;
+            const uint16_t* tv = p.tail_v + (size_t)bh * p.tail_stride * D + 4 * qd;
             for (int t = tgi; t < p.tail_len; t += TGR) {
                 float vf[4];
 #pragma unroll

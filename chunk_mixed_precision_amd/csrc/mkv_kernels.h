@@ -100,9 +100,10 @@ struct AttnParams {
     int B, Hkv, Hq, C;
     int G;                  // workgroups launched (the device may use fewer)
     float* part;            // [B*Hkv + G][g][d+4]: o[d], m (log2 domain), l, 0, 0
-    const uint16_t* tail_k; // [B][Hkv][tail_len][d] or NULL
+    const uint16_t* tail_k; // [B][Hkv][tail_stride][d] or NULL; tokens 0..tail_len-1 are used
     const uint16_t* tail_v;
     int tail_len;
+    int tail_stride;        // tokens between consecutive (sequence, head) rows of the tail
     float* out;             // [B][Hq][d]
     float qscale;           // log2(e) / sqrt(d)
 };
@@ -113,6 +114,8 @@ hipError_t launch_vote(const VoteParams& vp, int n_new, hipStream_t st);
 hipError_t launch_reorder(const ReorderParams& rp, int B, hipStream_t st);
 hipError_t launch_quant(const QuantParams& qp, int D, int ngroups, hipStream_t st);
 hipError_t launch_similarity(const SimParams& sp, hipStream_t st);
+hipError_t launch_copy_rows(const void* src, size_t spitch, void* dst, size_t dpitch, size_t row_bytes, int rows,
+                            hipStream_t st);
 hipError_t launch_attention(const AttnParams& ap, int D, int HB, hipStream_t st);
 
 }  // namespace mkv

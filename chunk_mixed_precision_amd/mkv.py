@@ -35,7 +35,7 @@ MKV_OP_SIMILARITY = 3
 
 EXPORTED = (
     "mkv_route_chunks", "mkv_select_chunks_by_similarity", "mkv_quantize_pack_kv",
-    "mkv_mixed_kv_decode_attention",
+    "mkv_mixed_kv_decode_attention", "mkv_append_tail_rows", "mkv_grow_pool",
     "mkv_workspace_bytes", "mkv_group_bytes", "mkv_pool_bytes",
     "mkv_status_string", "mkv_last_hip_error", "mkv_version",
 )
@@ -80,8 +80,12 @@ def lib() -> ctypes.CDLL:
         L.mkv_quantize_pack_kv.argtypes = [vp, vp, i, i, ctypes.POINTER(MkvTables),
                                            ctypes.POINTER(MkvCache), vp]
         L.mkv_quantize_pack_kv.restype = i
-        L.mkv_mixed_kv_decode_attention.argtypes = [vp, i, ctypes.POINTER(MkvCache), vp, vp, i,
+        L.mkv_mixed_kv_decode_attention.argtypes = [vp, i, ctypes.POINTER(MkvCache), vp, vp, i, i,
                                                     vp, vp, sz, vp]
+        L.mkv_append_tail_rows.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+        L.mkv_append_tail_rows.restype = i
+        L.mkv_grow_pool.argtypes = [vp, vp, i, i, i, i, i, i, i, vp]
+        L.mkv_grow_pool.restype = i
         L.mkv_mixed_kv_decode_attention.restype = i
         L.mkv_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int)]
         L.mkv_workspace_bytes.restype = sz
@@ -108,7 +112,13 @@ def _check(status: int, what: str):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor's data.  The C ABI takes dense row-major
+    arrays, so a strided view is refused rather than read as if dense."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("the C ABI needs contiguous tensors (call .contiguous() on views)")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream=None):
@@ -226,6 +236,24 @@ def select_chunks_by_similarity(tables: RouteTables, C: int, x: torch.Tensor, qe
     _check(st, "mkv_select_chunks_by_similarity")
 
 
+def append_tail_rows(a_new: torch.Tensor, a_tail: torch.Tensor, pos: int, b_new: torch.Tensor = None,
+                     b_tail: torch.Tensor = None, stream=None):
+    """mkv_append_tail_rows: a_new [..., W] (rows = all leading dims) into
+    token `pos` of a_tail [..., S, W]; the same for the b pair if given."""
+    W = a_new.shape[-1]
+    rows = a_new.numel() // W
+    st = lib().mkv_append_tail_rows(_ptr(a_new), _ptr(b_new), _ptr(a_tail), _ptr(b_tail), rows, W,
+                                    a_tail.shape[-2], pos, _stream(stream))
+    _check(st, "mkv_append_tail_rows")
+
+
+def grow_pool(src: torch.Tensor, dst: torch.Tensor, bits: int, B: int, Hkv: int, cap_old: int, cap_new: int,
+              d: int, C: int, stream=None):
+    """mkv_grow_pool: re-lay a pool of cap_old slots into one of cap_new."""
+    st = lib().mkv_grow_pool(_ptr(src), _ptr(dst), bits, B, Hkv, cap_old, cap_new, d, C, _stream(stream))
+    _check(st, "mkv_grow_pool")
+
+
 def quantize_pack_kv(k: torch.Tensor, v: torch.Tensor, tables: RouteTables, cache: PackedCache,
                      chunk_offset: int = 0, stream=None):
     """mkv_quantize_pack_kv: k, v [B, Hkv, T, d] fp16 (T = new chunks * C)."""
@@ -245,17 +273,21 @@ def attention_workspace(B: int, Hq: int, cache: "PackedCache", device="cuda") ->
 
 def mixed_kv_decode_attention(q: torch.Tensor, cache: PackedCache, out: torch.Tensor = None,
                               tail_k: torch.Tensor = None, tail_v: torch.Tensor = None,
-                              workspace: torch.Tensor = None, stream=None) -> torch.Tensor:
-    """mkv_mixed_kv_decode_attention: q [B, Hq, d] fp16 -> out [B, Hq, d] f32."""
+                              tail_len: int = None, workspace: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """mkv_mixed_kv_decode_attention: q [B, Hq, d] fp16 -> out [B, Hq, d] f32.
+    tail_k, tail_v: [B, Hkv, S, d] fp16 tails of S rows; tokens 0 .. tail_len-1
+    of each row are attended (tail_len defaults to S)."""
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = attention_workspace(B, Hq, cache, q.device)
-    tail_len = 0 if tail_k is None else tail_k.shape[2]
+    stride = 0 if tail_k is None else tail_k.shape[2]
+    if tail_len is None:
+        tail_len = stride
     cc = cache.c()
     st = lib().mkv_mixed_kv_decode_attention(_ptr(q), Hq, ctypes.byref(cc), _ptr(tail_k), _ptr(tail_v),
-                                             tail_len, _ptr(out), _ptr(workspace),
+                                             tail_len, stride, _ptr(out), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "mkv_mixed_kv_decode_attention")
     return out

@@ -75,6 +75,20 @@ def query_embedding(w: Workload, batch: int = None, layer: int = 0) -> torch.Ten
     return z.to(torch.bfloat16)
 
 
+def decode_tokens(w: Workload, steps: int, device, layer: int = 0):
+    """Per-step inputs of a streaming decode, drawn on the device: hidden
+    states x [steps, B, D] bf16 (iid N(0,1)), k, v [steps, B, Hkv, d] fp16
+    and q [steps, B, Hq, d] fp16 (N(0,1); outlier key columns scaled as in
+    ``kv``)."""
+    g = _gen(w.seed, 12, layer, device)
+    x = torch.randn((steps, w.B, w.D), generator=g, device=device).to(torch.bfloat16)
+    k = torch.randn((steps, w.B, w.Hkv, w.d), generator=g, device=device)
+    v = torch.randn((steps, w.B, w.Hkv, w.d), generator=g, device=device)
+    k.mul_(outlier_mask(w).to(device)[None, None])
+    q = torch.randn((steps, w.B, w.Hq, w.d), generator=g, device=device)
+    return x, k.to(torch.float16), v.to(torch.float16), q.to(torch.float16)
+
+
 def outlier_mask(w: Workload) -> torch.Tensor:
     """[Hkv, d] float multiplier for the key columns (KIVI-style outlier
     channels): channels 0..k-1 of every head, or a seeded set of columns."""

@@ -247,7 +247,11 @@ int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T,
  * summation order (not the result beyond rounding) can differ between calls.
  *
  *   q_fp16      [B][Hq][d] fp16
- *   tail_k/v    [B][Hkv][tail_len][d] fp16, or NULL when tail_len == 0
+ *   tail_k/v    [B][Hkv][tail_stride][d] fp16, tokens 0 .. tail_len-1 of
+ *               each row used; NULL when tail_len == 0
+ *   tail_stride tokens between consecutive (sequence, head) rows of the
+ *               tail, >= tail_len; 0 means tail_len (a packed tail).  A
+ *               decode loop keeps a tail buffer of C rows and passes C.
  *   out         [B][Hq][d] fp32
  *   workspace   at least mkv_workspace_bytes(MKV_OP_ATTENTION, ...) bytes
  *               (tile partials; no initial contents needed).  Calls that
@@ -261,8 +265,33 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq,
                                   const mkv_cache* cache,
                                   const void* tail_k_fp16,
                                   const void* tail_v_fp16, int tail_len,
-                                  float* out, void* workspace,
+                                  int tail_stride, float* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Streaming decode helpers: the step either side of the path (MoQAE
+ * "Overall framework": the context is cut into equal chunks as it grows).
+ * Tokens of a partial chunk wait in an fp16 tail that attention reads
+ * directly; a full tail is routed, quantized and appended as one chunk.
+ *
+ * mkv_append_tail_rows: copy row r of `a_new` (and of `b_new`, if not NULL)
+ * into row r, token `pos` of the tail `a_tail` (`b_tail`), for r < rows:
+ *   a_new, b_new    [rows][width] 2-byte elements (fp16 K/V of one token
+ *                   per (sequence, head): rows = B*Hkv, width = d; or bf16
+ *                   hidden states: rows = B, width = D)
+ *   a_tail, b_tail  [rows][tail_stride][width]
+ * 0 <= pos < tail_stride.  width % 8 == 0; buffers 16-byte aligned.
+ *
+ * mkv_grow_pool: copy a pool of `bits` laid out for cap_old slots per
+ * (sequence, head) into a pool laid out for cap_new >= cap_old slots (see
+ * mkv_cache).  Slots cap_old .. cap_new-1 of dst are left as they were.
+ * src and dst must not overlap.
+ * ---------------------------------------------------------------------- */
+int mkv_append_tail_rows(const void* a_new, const void* b_new, void* a_tail,
+                         void* b_tail, int rows, int width, int tail_stride,
+                         int pos, void* stream);
+int mkv_grow_pool(const void* src, void* dst, int bits, int B, int Hkv,
+                  int cap_old, int cap_new, int d, int C, void* stream);
 
 /* ---- helpers -------------------------------------------------------------
  * mkv_workspace_bytes: scratch needed by an op.

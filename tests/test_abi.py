@@ -127,10 +127,10 @@ def test_quantize_argument_errors():
     assert quant(cache=c) == E.MKV_ERR_ARG
 
 
-def attn(Hq=2, cache=None, tail_len=0, tk=None, tv=None, out=0x700, ws=None, wsb=0, q=0x600):
+def attn(Hq=2, cache=None, tail_len=0, tk=None, tv=None, out=0x700, ws=None, wsb=0, q=0x600, stride=0):
     cache = cache or _cache()
-    return mkv.lib().mkv_mixed_kv_decode_attention(q, Hq, ctypes.byref(cache), tk, tv, tail_len, out, ws, wsb,
-                                                   None)
+    return mkv.lib().mkv_mixed_kv_decode_attention(q, Hq, ctypes.byref(cache), tk, tv, tail_len, stride, out, ws,
+                                                   wsb, None)
 
 
 def test_attention_argument_errors():
@@ -142,6 +142,7 @@ def test_attention_argument_errors():
     assert attn(cache=_cache(d=256)) == E.MKV_ERR_UNSUPPORTED
     assert attn(tail_len=5) == E.MKV_ERR_ARG                    # tail pointers missing
     assert attn(tail_len=4096, tk=0x800, tv=0x900) == E.MKV_ERR_ARG
+    assert attn(tail_len=5, tk=0x800, tv=0x900, stride=4) == E.MKV_ERR_ARG   # stride below tail_len
     assert attn() == E.MKV_ERR_WORKSPACE
     assert attn(ws=0x9000, wsb=64) == E.MKV_ERR_WORKSPACE
 
@@ -174,3 +175,18 @@ def test_similarity_selection_argument_errors():
     assert select() == E.MKV_ERR_WORKSPACE                       # no workspace
     assert select(ws=0x9000, wsb=16) == E.MKV_ERR_WORKSPACE      # too small
     assert mkv.workspace_bytes_similarity(2, 1024, 4096, 256) == 2 * 4 * 8 * 16
+
+
+def test_stream_helper_argument_errors():
+    L, E = mkv.lib(), mkv
+    app = L.mkv_append_tail_rows
+    assert app(None, None, 0x200, None, 4, 128, 32, 0, None) == E.MKV_ERR_ARG
+    assert app(0x100, 0x300, 0x200, None, 4, 128, 32, 0, None) == E.MKV_ERR_ARG      # b pair half given
+    assert app(0x108, None, 0x200, None, 4, 128, 32, 0, None) == E.MKV_ERR_ARG       # misaligned
+    assert app(0x100, None, 0x200, None, 4, 128, 32, 32, None) == E.MKV_ERR_ARG      # pos >= stride
+    assert app(0x100, None, 0x200, None, 4, 100, 32, 0, None) == E.MKV_ERR_UNSUPPORTED
+    grow = L.mkv_grow_pool
+    assert grow(0x1000, 0x100000, 4, 1, 2, 3, 2, 128, 128, None) == E.MKV_ERR_ARG   # shrinking
+    assert grow(0x1000, 0x100000, 8, 1, 2, 1, 2, 128, 128, None) == E.MKV_ERR_UNSUPPORTED
+    assert grow(0x1000, 0x2000, 4, 1, 2, 1, 2, 128, 128, None) == E.MKV_ERR_ARG     # overlap
+    assert grow(None, 0x100000, 4, 1, 2, 1, 2, 128, 128, None) == E.MKV_ERR_ARG
