@@ -54,6 +54,10 @@ the design notes):
       chunks matter more to the query and keep more bits).  Routing freezing
       may pin chunk 0 as for the router.  parity unpinned against the
       authors' search (no code or constants exist).
+  R10 Chunked prefill: a chunk of P new tokens is attended before it is
+      quantized.  Query i of the chunk sees every cached token (dequantized)
+      and the new chunk's own fp16 tokens 0..i (causal), in ordinary softmax
+      attention.
 """
 from __future__ import annotations
 
@@ -319,6 +323,21 @@ def select_by_similarity(x_bits: np.ndarray, qe_bits: np.ndarray, chunk: int, ta
     e = similarity_experts(sim, tau_hi, tau_lo, freeze_first)
     perm, rank, seg = reorder(e)
     return sim, e, perm, rank, seg
+
+
+def prefill_attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray,
+                      k_new: np.ndarray, v_new: np.ndarray) -> np.ndarray:
+    """Chunked-prefill attention of one (sequence, query head), float64
+    (reading R10).  q [P, d] queries of the new chunk, k_hat/v_hat [T, d]
+    the dequantized cache, k_new/v_new [P, d] the chunk's own keys/values.
+    Returns [P, d]: row i attends to the cache and new tokens 0..i."""
+    P = q.shape[0]
+    out = np.zeros((P, q.shape[1]))
+    for i in range(P):
+        k = np.concatenate([k_hat, k_new[:i + 1]])
+        v = np.concatenate([v_hat, v_new[:i + 1]])
+        out[i] = attention(q[i], k, v)
+    return out
 
 
 def route(x_bits: np.ndarray, w12_bits: np.ndarray, w3: np.ndarray,

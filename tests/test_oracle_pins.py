@@ -508,3 +508,68 @@ def test_pins_catch_planted_similarity_mistakes(variant):
                                                                                           orc.similarity_experts)
     with pytest.raises(AssertionError):
         check_similarity_on_cases(sim_fn, ex_fn)
+
+
+# ---------------------------------------------------------------- chunked prefill attention
+def test_prefill_attention_closed_forms():
+    """Reading R10 (ordinary attention; a chunk's own tokens causally)."""
+    rng = np.random.default_rng(11)
+    d, P, T = 16, 6, 5
+    q = rng.standard_normal((P, d))
+    kn, vn = rng.standard_normal((P, d)), rng.standard_normal((P, d))
+    # no cache: the first query sees only its own token
+    o = orc.prefill_attention(q, np.zeros((0, d)), np.zeros((0, d)), kn, vn)
+    assert np.allclose(o[0], vn[0], atol=0, rtol=0)
+    # equal keys: every visible value weighs the same
+    kh, vh = np.ones((T, d)), rng.standard_normal((T, d))
+    o = orc.prefill_attention(q, kh, vh, np.ones((P, d)), vn)
+    for i in range(P):
+        assert np.allclose(o[i], np.concatenate([vh, vn[:i + 1]]).mean(axis=0), atol=1e-13)
+    # causality: later tokens of the chunk never change earlier rows
+    kn2, vn2 = kn.copy(), vn.copy()
+    kn2[3:] += 5.0
+    vn2[3:] -= 7.0
+    kh, vh = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    a = orc.prefill_attention(q, kh, vh, kn, vn)
+    b = orc.prefill_attention(q, kh, vh, kn2, vn2)
+    assert np.array_equal(a[:3], b[:3]) and not np.allclose(a[3:], b[3:])
+
+
+def test_prefill_attention_matches_sdpa_with_mask():
+    import torch
+    rng = np.random.default_rng(12)
+    d, P, T = 32, 9, 14
+    q = rng.standard_normal((P, d))
+    kh, vh = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    kn, vn = rng.standard_normal((P, d)), rng.standard_normal((P, d))
+    mask = np.ones((P, T + P), dtype=bool)
+    mask[:, T:] = np.tril(np.ones((P, P), dtype=bool))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(np.concatenate([kh, kn]))[None],
+        torch.from_numpy(np.concatenate([vh, vn]))[None], attn_mask=torch.from_numpy(mask)[None])[0].numpy()
+    assert np.allclose(orc.prefill_attention(q, kh, vh, kn, vn), ref, atol=1e-12)
+
+
+def _prefill_variant(mistake):
+    def f(q, kh, vh, kn, vn):
+        P = q.shape[0]
+        out = np.zeros((P, q.shape[1]))
+        for i in range(P):
+            hi = P if mistake == "not_causal" else i
+            k = np.concatenate([kh, kn[:hi]])
+            v = np.concatenate([vh, vn[:hi]])
+            out[i] = orc.attention(q[i], k, v) if len(k) else 0.0
+        return out
+    return f
+
+
+@pytest.mark.parametrize("mistake", ["not_causal", "excludes_own_token"])
+def test_pins_catch_planted_prefill_mistakes(mistake):
+    rng = np.random.default_rng(13)
+    d, P = 8, 4
+    q, kn, vn = rng.standard_normal((P, d)), rng.standard_normal((P, d)), rng.standard_normal((P, d))
+    f = _prefill_variant(mistake)
+    with pytest.raises(AssertionError):
+        o = f(q, np.zeros((0, d)), np.zeros((0, d)), kn, vn)
+        assert np.allclose(o[0], vn[0], atol=0, rtol=0)
+        assert np.allclose(o, orc.prefill_attention(q, np.zeros((0, d)), np.zeros((0, d)), kn, vn))
