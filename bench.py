@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA, published
 
 
 def parse():
@@ -54,6 +55,9 @@ def parse():
     ap.add_argument("--routing-ablation", type=int, default=0, metavar="L",
                     help="also time L-layer steps with routing sharing (one route, L x quantize + attend) "
                          "and without it (every layer routes its own hidden states)")
+    ap.add_argument("--prefill-chunk", type=int, default=256, metavar="P",
+                    help="also time chunked-prefill attention of P new tokens per sequence over the same "
+                         "cache (0 disables)")
     ap.add_argument("--decode-steps", type=int, default=0, metavar="N",
                     help="also time N streaming-decode steps (one token per sequence, full chunks routed, "
                          "quantized and appended) on the grouped-query workload")
@@ -333,6 +337,39 @@ def main():
     t_sim = np.array([a.elapsed_time(b) for a, b in ev_sim]) * 1e-3
     sim_bytes = w.B * w.T * w.D * 2 + w.B * w.D * 2 + w.B * w.n * (1 + 4 + 4)
 
+    # chunked prefill: P new tokens per sequence attend over the same caches (rotated) and causally
+    # over themselves, on the matrix cores
+    pre = None
+    if args.prefill_chunk > 0:
+        Pn = args.prefill_chunk
+        gq = torch.Generator(device=dev)
+        gq.manual_seed(w.seed * 100 + 55)
+        pq = torch.randn((w.B, w.Hq, Pn, w.d), generator=gq, device=dev).to(torch.float16)
+        pkn = torch.randn((w.B, w.Hkv, Pn, w.d), generator=gq, device=dev).to(torch.float16)
+        pvn = torch.randn((w.B, w.Hkv, Pn, w.d), generator=gq, device=dev).to(torch.float16)
+        pout = torch.empty((w.B, w.Hq, Pn, w.d), dtype=torch.float32, device=dev)
+        pws = torch.empty(mkv.workspace_bytes_prefill(w.B, w.Hq, Pn, w.d, w.C, caps), dtype=torch.uint8, device=dev)
+        for i in range(3):
+            mkv.mixed_kv_prefill_attention(pq, caches[i % R], pkn, pvn, out=pout, workspace=pws)
+        ev_pre = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
+        for i in range(nev):
+            ev_pre[i][0].record()
+            mkv.mixed_kv_prefill_attention(pq, caches[i % R], pkn, pvn, out=pout, workspace=pws)
+            ev_pre[i][1].record()
+        torch.cuda.synchronize()
+        t_pre = float(np.mean([a.elapsed_time(b) for a, b in ev_pre])) * 1e-3
+        ctx = w.T
+        pre_flop = 4.0 * w.B * w.Hq * Pn * w.d * (ctx + (Pn + 1) / 2.0)
+        pre_bytes = (configs.effective_attention_bytes(w, seg) - w.B * w.Hq * w.d * 6
+                     + w.B * w.Hq * Pn * w.d * (2 + 4) + 2 * w.B * w.Hkv * Pn * w.d * 2)
+        pre = {"P": Pn, "us": round(t_pre * 1e6, 2),
+               "roofline": {"bound": "mfma", "achieved": round(pre_flop / t_pre / 1e12, 2),
+                            "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(pre_flop / t_pre / 1e12 / FP16_PEAK_TFLOPS, 4),
+                            "flop_per_launch": pre_flop},
+               "effective_gbs": round(pre_bytes / t_pre / 1e9, 1), "bytes_per_launch": pre_bytes}
+        del pq, pkn, pvn, pout, pws
+
     t_pack = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
     t_route = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
     t_attn = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(nev)]) * 1e-3
@@ -387,6 +424,7 @@ def main():
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(sim_bytes / float(t_sim.mean()) / 1e9 / HBM_PEAK_GBS, 4),
                              "bytes_per_launch": sim_bytes}},
+            "prefill_attend": pre,
             "attend": {"us": round(a_mean * 1e6, 2), "us_p10": round(float(np.percentile(t_attn, 10)) * 1e6, 2),
                        "us_p90": round(float(np.percentile(t_attn, 90)) * 1e6, 2), "bytes": attn_bytes,
                        "traffic": None if traffic is None else {

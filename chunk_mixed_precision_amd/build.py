@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmkv.so")
 
-SOURCES = ["api.hip", "route.hip", "select.hip", "quant.hip", "attn.hip", "stream.hip"]
+SOURCES = ["api.hip", "route.hip", "select.hip", "quant.hip", "attn.hip", "prefill.hip", "stream.hip"]
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 VALU instructions anywhere in device code

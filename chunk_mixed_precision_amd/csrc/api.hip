@@ -39,6 +39,19 @@ inline int attn_workgroups(int B, int Hkv, int d, const int* cap, int C) {
     return (int)g;
 }
 
+// Chunked prefill: splits of each (sequence, query head)'s cached group
+// blocks, enough that the grid covers about two workgroups per CU, none
+// shorter than 4 group blocks (counted at capacity).
+inline int prefill_splits(int B, int Hq, int P, const int* cap, int C) {
+    const long long tiles = (long long)B * Hq * ((P + 127) / 128);
+    long long ns = (512 + tiles - 1) / tiles;
+    const long long gcap = ((long long)cap[0] + cap[1] + cap[2]) * (C / mkv::kGroup);
+    if (ns > gcap / 4) ns = gcap / 4;
+    if (ns > 32) ns = 32;
+    if (ns < 1) ns = 1;
+    return (int)ns;
+}
+
 inline bool valid_cache(const mkv_cache* c) {
     if (!c) return false;
     if (c->B <= 0 || c->Hkv <= 0 || c->C <= 0 || c->d <= 0) return false;
@@ -98,6 +111,12 @@ size_t mkv_workspace_bytes(int op, int a, int b, int c, int e, int f, const int*
         if (B <= 0 || T <= 0 || D <= 0 || C <= 0 || T % C) return 0;
         const size_t ds = ((size_t)D + mkv::kSimSlice - 1) / mkv::kSimSlice;
         return (size_t)B * (T / C) * ds * 16;
+    }
+    if (op == MKV_OP_PREFILL) {
+        const int B = a, Hq = b, P = c, d = e, C = f;
+        if (!caps || B <= 0 || Hq <= 0 || P <= 0 || (d != 64 && d != 128) || C <= 0 || C % 32) return 0;
+        const int ns = prefill_splits(B, Hq, P, caps, C);
+        return (size_t)B * Hq * P * ns * (d + 4) * sizeof(float) + 16;
     }
     if (op == MKV_OP_ATTENTION) {
         const int B = a, Hq = b, Hkv = c, d = e, C = f;
@@ -265,6 +284,35 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq, const mkv_cache* c
     ap.out = out;
     ap.qscale = (float)(1.4426950408889634 / sqrt((double)cache->d));
     return hip_status(mkv::launch_attention(ap, cache->d, g, (hipStream_t)stream));
+}
+
+int mkv_mixed_kv_prefill_attention(const void* q_fp16, int Hq, int P, const mkv_cache* cache,
+                                   const void* k_new_fp16, const void* v_new_fp16, float* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!q_fp16 || !out || !k_new_fp16 || !v_new_fp16) return MKV_ERR_ARG;
+    if (!aligned16(q_fp16) || !aligned16(out) || !aligned16(k_new_fp16) || !aligned16(v_new_fp16)) return MKV_ERR_ARG;
+    if (!valid_cache(cache)) return MKV_ERR_ARG;
+    int s = check_cache_shape(cache);
+    if (s) return s;
+    if (Hq <= 0 || Hq % cache->Hkv != 0 || P <= 0) return MKV_ERR_ARG;
+    if (P > 65535 || (long long)cache->B * Hq > 65535) return MKV_ERR_UNSUPPORTED;
+    const size_t need = mkv_workspace_bytes(MKV_OP_PREFILL, cache->B, Hq, P, cache->d, cache->C, cache->cap);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return MKV_ERR_WORKSPACE;
+    mkv::PrefillParams pp{};
+    pp.q = static_cast<const uint16_t*>(q_fp16);
+    for (int k = 0; k < 3; ++k) {
+        pp.pool[k] = static_cast<const uint8_t*>(cache->pool[k]);
+        pp.cap[k] = cache->cap[k];
+    }
+    pp.seg_count = cache->seg_count;
+    pp.k_new = static_cast<const uint16_t*>(k_new_fp16);
+    pp.v_new = static_cast<const uint16_t*>(v_new_fp16);
+    pp.part = static_cast<float*>(workspace);
+    pp.out = out;
+    pp.B = cache->B; pp.Hq = Hq; pp.Hkv = cache->Hkv; pp.C = cache->C; pp.P = P;
+    pp.NS = prefill_splits(cache->B, Hq, P, cache->cap, cache->C);
+    pp.qscale = (float)(1.4426950408889634 / sqrt((double)cache->d));
+    return hip_status(mkv::launch_prefill(pp, cache->d, (hipStream_t)stream));
 }
 
 int mkv_append_tail_rows(const void* a_new, const void* b_new, void* a_tail, void* b_tail, int rows, int width,

@@ -57,6 +57,20 @@ struct SimParams {
     int freeze_first;
 };
 
+// ---------------------------------------------------------------- chunked prefill
+struct PrefillParams {
+    const uint16_t* q;      // [B][Hq][P][d] fp16 queries of the new chunk
+    const uint8_t* pool[3];
+    int cap[3];
+    const int32_t* seg_count;
+    const uint16_t* k_new;  // [B][Hkv][P][d] fp16: the chunk's own keys / values
+    const uint16_t* v_new;
+    float* part;            // [B][Hq][P][NS][d+4]: o[d], m (log2 domain), l, 0, 0
+    float* out;             // [B][Hq][P][d]
+    int B, Hq, Hkv, C, P, NS;
+    float qscale;           // log2(e) / sqrt(d)
+};
+
 // ---------------------------------------------------------------- quantize
 struct QuantParams {
     const uint16_t* k;      // [B][Hkv][T][d] fp16 bits
@@ -114,6 +128,7 @@ hipError_t launch_vote(const VoteParams& vp, int n_new, hipStream_t st);
 hipError_t launch_reorder(const ReorderParams& rp, int B, hipStream_t st);
 hipError_t launch_quant(const QuantParams& qp, int D, int ngroups, hipStream_t st);
 hipError_t launch_similarity(const SimParams& sp, hipStream_t st);
+hipError_t launch_prefill(const PrefillParams& pp, int D, hipStream_t st);
 hipError_t launch_copy_rows(const void* src, size_t spitch, void* dst, size_t dpitch, size_t row_bytes, int rows,
                             hipStream_t st);
 hipError_t launch_attention(const AttnParams& ap, int D, int HB, hipStream_t st);

@@ -32,10 +32,11 @@ MKV_APPEND = 0x4
 MKV_OP_ROUTE = 1
 MKV_OP_ATTENTION = 2
 MKV_OP_SIMILARITY = 3
+MKV_OP_PREFILL = 4
 
 EXPORTED = (
     "mkv_route_chunks", "mkv_select_chunks_by_similarity", "mkv_quantize_pack_kv",
-    "mkv_mixed_kv_decode_attention", "mkv_append_tail_rows", "mkv_grow_pool",
+    "mkv_mixed_kv_decode_attention", "mkv_mixed_kv_prefill_attention", "mkv_append_tail_rows", "mkv_grow_pool",
     "mkv_workspace_bytes", "mkv_group_bytes", "mkv_pool_bytes",
     "mkv_status_string", "mkv_last_hip_error", "mkv_version",
 )
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.mkv_quantize_pack_kv.restype = i
         L.mkv_mixed_kv_decode_attention.argtypes = [vp, i, ctypes.POINTER(MkvCache), vp, vp, i, i,
                                                     vp, vp, sz, vp]
+        L.mkv_mixed_kv_prefill_attention.argtypes = [vp, i, i, ctypes.POINTER(MkvCache), vp, vp, vp, vp, sz, vp]
+        L.mkv_mixed_kv_prefill_attention.restype = i
         L.mkv_append_tail_rows.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
         L.mkv_append_tail_rows.restype = i
         L.mkv_grow_pool.argtypes = [vp, vp, i, i, i, i, i, i, i, vp]
@@ -234,6 +237,29 @@ def select_chunks_by_similarity(tables: RouteTables, C: int, x: torch.Tensor, qe
                                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                                _stream(stream))
     _check(st, "mkv_select_chunks_by_similarity")
+
+
+def workspace_bytes_prefill(B: int, Hq: int, P: int, d: int, C: int, caps: Sequence[int]) -> int:
+    arr = (ctypes.c_int * 3)(*[int(c) for c in caps])
+    return int(lib().mkv_workspace_bytes(MKV_OP_PREFILL, B, Hq, P, d, C, arr))
+
+
+def mixed_kv_prefill_attention(q: torch.Tensor, cache: PackedCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                               out: torch.Tensor = None, workspace: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """mkv_mixed_kv_prefill_attention: q [B, Hq, P, d] fp16, k_new/v_new
+    [B, Hkv, P, d] fp16 -> out [B, Hq, P, d] f32."""
+    B, Hq, P, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, P, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes_prefill(B, Hq, P, d, cache.C, cache.caps), dtype=torch.uint8,
+                                device=q.device)
+    cc = cache.c()
+    st = lib().mkv_mixed_kv_prefill_attention(_ptr(q), Hq, P, ctypes.byref(cc), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                              _stream(stream))
+    _check(st, "mkv_mixed_kv_prefill_attention")
+    return out
 
 
 def append_tail_rows(a_new: torch.Tensor, a_tail: torch.Tensor, pos: int, b_new: torch.Tensor = None,

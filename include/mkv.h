@@ -71,6 +71,7 @@ extern "C" {
 #define MKV_OP_ROUTE      1
 #define MKV_OP_ATTENTION  2
 #define MKV_OP_SIMILARITY 3
+#define MKV_OP_PREFILL    4
 
 /* Routing tables of a batch of sequences (routing sharing: one table serves
  * every layer and head).  All arrays are device memory, row stride n_max:
@@ -269,6 +270,32 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq,
                                   size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * 3b. mkv_mixed_kv_prefill_attention — chunked prefill over the mixed cache:
+ *    a chunk of P new tokens attends before it is quantized (MoQAE "Overall
+ *    framework": ordinary attention; Cocktail abstract: chunk-level
+ *    computation over the bitwidth segments).
+ *
+ * For each sequence b, query head hq (KV head h = hq / (Hq/Hkv)) and query
+ * i < P: out[b][hq][i] = softmax(q k^T / sqrt(d)) v over every cached token
+ * of (b, h) and the new tokens 0..i of k_new/v_new (causal).  Cached values
+ * are dequantized to fp16 tiles and multiplied on the matrix cores with fp32
+ * accumulation; the splits of the cache are merged with a log-sum-exp
+ * combine.
+ *
+ *   q_fp16      [B][Hq][P][d] fp16
+ *   k_new/v_new [B][Hkv][P][d] fp16: the chunk's own keys and values
+ *   out         [B][Hq][P][d] fp32
+ *   workspace   at least mkv_workspace_bytes(MKV_OP_PREFILL, ...) bytes
+ * Limits: d in {64, 128}; Hq % Hkv == 0; 1 <= P <= 65535; B*Hq <= 65535.
+ * ---------------------------------------------------------------------- */
+int mkv_mixed_kv_prefill_attention(const void* q_fp16, int Hq, int P,
+                                   const mkv_cache* cache,
+                                   const void* k_new_fp16,
+                                   const void* v_new_fp16, float* out,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
  * Streaming decode helpers: the step either side of the path (MoQAE
  * "Overall framework": the context is cut into equal chunks as it grows).
  * Tokens of a partial chunk wait in an fp16 tail that attention reads
@@ -299,6 +326,8 @@ int mkv_grow_pool(const void* src, void* dst, int bits, int B, int Hkv,
  *   MKV_OP_ATTENTION: a = B, b = Hq, c = Hkv, e = d, f = C, and `cache_caps`
  *                     points to the cache's cap[3] (host memory)
  *   MKV_OP_SIMILARITY: a = B, b = T, c = D, e = C (f, cache_caps unused)
+ *   MKV_OP_PREFILL:   a = B, b = Hq, c = P, e = d, f = C, and `cache_caps`
+ *                     points to the cache's cap[3] (host memory)
  * Returns 0 for an unknown op or invalid sizes.                          */
 size_t mkv_workspace_bytes(int op, int a, int b, int c, int e, int f,
                            const int* cache_caps);
