@@ -40,11 +40,11 @@ inline int attn_workgroups(int B, int Hkv, int d, const int* cap, int C) {
 }
 
 // Chunked prefill: splits of each (sequence, query head)'s cached group
-// blocks, enough that the grid covers about two workgroups per CU, none
-// shorter than 4 group blocks (counted at capacity).
+// blocks, enough that the grid covers about one 8-wavefront workgroup per CU,
+// none shorter than 4 group blocks (counted at capacity).
 inline int prefill_splits(int B, int Hq, int P, const int* cap, int C) {
-    const long long tiles = (long long)B * Hq * ((P + 127) / 128);
-    long long ns = (512 + tiles - 1) / tiles;
+    const long long tiles = (long long)B * Hq * ((P + 255) / 256);
+    long long ns = (256 + tiles - 1) / tiles;
     const long long gcap = ((long long)cap[0] + cap[1] + cap[2]) * (C / mkv::kGroup);
     if (ns > gcap / 4) ns = gcap / 4;
     if (ns > 32) ns = 32;

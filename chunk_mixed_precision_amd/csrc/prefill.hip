@@ -5,10 +5,10 @@
 // every cached token and the chunk's own fp16 tokens 0..i.
 //
 // Unlike a decode step this is a dense contraction (P queries x T tokens x
-// d), so it runs on the matrix cores.  A workgroup holds 128 queries of one
+// d), so it runs on the matrix cores.  A workgroup holds 256 queries of one
 // query head (32 per wavefront) and one split of the cached group blocks.
 // Each 32-token group block is dequantized once into LDS as fp16 -- keys
-// token-major, values channel-major -- and shared by the four wavefronts;
+// token-major, values channel-major -- and shared by the eight wavefronts;
 // each wavefront then computes S^T = K Q^T with v_mfma_f32_32x32x16_f16
 // (lane = query, so the online softmax is lane-local), and O^T += V^T P^T
 // with the probabilities fed from its own accumulator registers.  Splits are
@@ -25,9 +25,11 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // a 16-byte cell as a value type
 
-constexpr int PT = 256;                 // threads per workgroup
+constexpr int NWAVE = 8;                // wavefronts per workgroup (2 per SIMD)
+constexpr int PT = 64 * NWAVE;          // threads per workgroup
 constexpr int QPW = 32;                 // queries per wavefront
-constexpr int RING_CELLS = 3072;        // 48 KB ring of raw group blocks (16-byte cells)
+constexpr int QT = QPW * NWAVE;         // queries per workgroup
+constexpr int RING_CELLS = 6144;        // 96 KB ring of raw group blocks (16-byte cells)
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glob_void;
@@ -50,10 +52,20 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int D>
+struct PfTile {
+    _Float16 k[32][D + 8];                 // keys of a block, token-major (rows padded by 16 bytes)
+    _Float16 vt[D][36];                    // values, channel-major: 32 tokens + 4 pad (72-byte rows);
+                                           // the 4-token chunk c of channel ch sits at chunk
+                                           // c ^ vt_swz(ch), spreading the writes over the banks
+};
+
+// Chunk swizzle of the value tile: the channel's 32-channel group.
+__device__ __forceinline__ constexpr int vt_swz(int ch) { return (ch >> 5) & 7; }
+
+template <int D>
 struct PfLds {
     u32x4 ring[RING_CELLS];                // raw group blocks in flight (slots sized per bitwidth)
-    _Float16 k[32][D + 8];                 // keys of the block, token-major (rows padded by 16 bytes)
-    _Float16 vt[D][36];                    // values, channel-major: 32 tokens + 4 pad (72-byte rows)
+    PfTile<D> tile[2];                     // fp16 blocks: one being consumed, one being filled
 };
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -68,7 +80,7 @@ __device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
 // for the values (gathered from the four lane slots that hold tokens
 // 4m .. 4m+3 of a value group).
 template <int D, int BITS>
-__device__ __forceinline__ void dequant_block(PfLds<D>& s, const u32x4* raw) {
+__device__ __forceinline__ void dequant_block(PfTile<D>& s, const u32x4* raw) {
     constexpr int S = D / 8, NG = D / 32;
     const int tid = threadIdx.x;
     if constexpr (BITS == 16) {
@@ -97,7 +109,8 @@ __device__ __forceinline__ void dequant_block(PfLds<D>& s, const u32x4* raw) {
                 const uint32_t a1 = (j & 1) ? hi16(w[1][wi]) : lo16(w[1][wi]);
                 const uint32_t a2 = (j & 1) ? hi16(w[2][wi]) : lo16(w[2][wi]);
                 const uint32_t a3 = (j & 1) ? hi16(w[3][wi]) : lo16(w[3][wi]);
-                *reinterpret_cast<uint2*>(&s.vt[ch + j][4 * m]) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+                *reinterpret_cast<uint2*>(&s.vt[ch + j][4 * (m ^ vt_swz(ch + j))]) =
+                    make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
             }
         }
     } else {
@@ -151,7 +164,8 @@ __device__ __forceinline__ void dequant_block(PfLds<D>& s, const u32x4* raw) {
                 float x[4];
 #pragma unroll
                 for (int tq = 0; tq < 4; ++tq) x[tq] = __builtin_fmaf((float)((wd[tq] >> sh) & MASK), sv[tq], mv[tq]);
-                *reinterpret_cast<uint2*>(&s.vt[ch + j][4 * mm]) = make_uint2(pack_h2(x[0], x[1]), pack_h2(x[2], x[3]));
+                *reinterpret_cast<uint2*>(&s.vt[ch + j][4 * (mm ^ vt_swz(ch + j))]) =
+                    make_uint2(pack_h2(x[0], x[1]), pack_h2(x[2], x[3]));
             }
         }
     }
@@ -174,7 +188,7 @@ struct PfState {
 // `causal`, token j of the block is new-chunk position base + j, visible to
 // query qp when base + j <= qp < P.
 template <int D>
-__device__ __forceinline__ void pf_block(PfState<D>& w, const PfLds<D>& s, float qscale, bool causal, int base,
+__device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, float qscale, bool causal, int base,
                                          int qp, int P) {
     const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
     f32x16 st;
@@ -186,10 +200,11 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfLds<D>& s, float
         st = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w.qf[ks], st, 0, 0, 0);
     }
     // st[r]: token 8(r>>2) + 4lh + (r&3) of the block, query qp
+    // raw scores; the scale (> 0) is applied inside the exponent's fma
     float mloc = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        float x = st[r] * qscale;
+        float x = st[r];
         if (causal) {
             const int tp = base + 8 * (r >> 2) + 4 * lh + (r & 3);
             if (tp > qp || tp >= P) x = -INFINITY;
@@ -197,30 +212,37 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfLds<D>& s, float
         st[r] = x;
         mloc = fmaxf(mloc, x);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * qscale;
     const float mn = fmaxf(w.m, mloc);
     const float alpha = (mn == -INFINITY) ? 1.f : exp2_fast(w.m - mn);
     float ps = 0.f;
     f16x8 pf0, pf1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const float pr = (mn == -INFINITY) ? 0.f : exp2_fast(st[r] - mn);
+        const float pr = (mn == -INFINITY) ? 0.f : exp2_fast(__builtin_fmaf(st[r], qscale, -mn));
         ps += pr;
         if (r < 8) pf0[r] = (_Float16)pr;
         else pf1[r - 8] = (_Float16)pr;
     }
     w.l = __builtin_fmaf(w.l, alpha, ps);
     w.m = mn;
+    // the running max rarely rises after the first blocks: rescale only then
+    // (alpha is exactly 1 for a lane whose max stayed)
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w.o[t][r] *= alpha;
+    }
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) w.o[t][r] *= alpha;
         // K step ks2 covers tokens 16ks2 + 8(j>>2) + 4lh + (j&3), j = 0..7: the
         // tokens of accumulator registers 8ks2 .. 8ks2+7 of this lane
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
-            const f16x4 v0 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][16 * ks2 + 4 * lh]);
-            const f16x4 v1 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][16 * ks2 + 8 + 4 * lh]);
+            // chunks 4ks2 + lh and 4ks2 + 2 + lh of channel 32t + lr (swizzle t)
+            const f16x4 v0 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][4 * ((4 * ks2 + lh) ^ (t & 7))]);
+            const f16x4 v1 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][4 * ((4 * ks2 + 2 + lh) ^ (t & 7))]);
             const f16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             w.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ks2 ? pf1 : pf0, w.o[t], 0, 0, 0);
         }
@@ -228,11 +250,12 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfLds<D>& s, float
 }
 
 // Group blocks [lo, hi) of one bitwidth segment.  Raw blocks stream into a
-// ring of NR slots by direct global->LDS loads issued NR-1 blocks ahead (one
+// ring of NR slots by direct global->LDS loads issued NR blocks ahead (one
 // block per iteration, re-reading the last block once the segment is
 // exhausted, so the number of loads in flight and hence every wait count is
-// fixed); each block is then dequantized into the fp16 tiles and consumed by
-// all four wavefronts.
+// fixed).  Iteration g dequantizes block g+1 into one fp16 tile while the
+// matrix cores consume block g from the other, with one barrier between
+// iterations.
 template <int D, int BITS>
 __device__ __forceinline__ void pf_segment(PfState<D>& w, PfLds<D>& s, const uint8_t* seg_base, int lo, int hi,
                                            float qscale, int qp, int P) {
@@ -242,7 +265,7 @@ __device__ __forceinline__ void pf_segment(PfState<D>& w, PfLds<D>& s, const uin
     constexpr int SLOT = LPW * PT;                 // cells per ring slot
     constexpr int NR = RING_CELLS / SLOT;          // ring slots
     constexpr int GC = (int)(group_bytes(BITS, D) / 16);
-    static_assert(NR >= 3 && (NR - 2) * LPW < 64, "ring depth");
+    static_assert(NR >= 3 && (NR - 1) * LPW < 64, "ring depth");
     if (lo >= hi) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const u32x4* seg = reinterpret_cast<const u32x4*>(seg_base);
@@ -252,28 +275,30 @@ __device__ __forceinline__ void pf_segment(PfState<D>& w, PfLds<D>& s, const uin
         u32x4* slot = s.ring + (g % NR) * SLOT;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const int c0 = (j * 4 + wave) * 64;    // this wavefront's 64 cells
+            const int c0 = (j * NWAVE + wave) * 64;    // this wavefront's 64 cells
             const int c = min(c0 + lane, NC - 1);
             __builtin_amdgcn_global_load_lds((glob_void*)(blk + c), (lds_void*)(slot + c0), 16, 0, 0);
         }
     };
 #pragma unroll
-    for (int i = 0; i < NR - 1; ++i) issue(lo + i);
+    for (int i = 0; i < NR; ++i) issue(lo + i);
+    __builtin_amdgcn_s_waitcnt(wait_vm((NR - 1) * LPW));      // this wavefront's part of block lo landed
+    lds_barrier();
+    dequant_block<D, BITS>(s.tile[lo & 1], s.ring + (lo % NR) * SLOT);
     for (int g = lo; g < hi; ++g) {
-        __builtin_amdgcn_s_waitcnt(wait_vm((NR - 2) * LPW));   // this wavefront's part of block g landed
-        __syncthreads();                                        // every part landed; the tiles are free
-        issue(g + NR - 1);                                      // into the slot of block g - 1
-        dequant_block<D, BITS>(s, s.ring + (g % NR) * SLOT);
-        lds_barrier();
-        pf_block<D>(w, s, qscale, false, 0, qp, P);
+        __builtin_amdgcn_s_waitcnt(wait_vm((NR - 2) * LPW));  // ... of block g+1 (or its stand-in)
+        lds_barrier();           // block g dequantized, block g+1 landed, block g-1 consumed
+        issue(g + NR);           // into the slot of block g, dequantized one iteration ago
+        if (g + 1 < hi) dequant_block<D, BITS>(s.tile[(g + 1) & 1], s.ring + ((g + 1) % NR) * SLOT);
+        pf_block<D>(w, s.tile[g & 1], qscale, false, 0, qp, P);
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));                     // the ring is reused by the next segment
-    __syncthreads();
+    lds_barrier();
 }
 
 }  // namespace
 
-// grid: x = query tile (128 queries), y = split, z = sequence * Hq + query head
+// grid: x = query tile (QT queries), y = split, z = sequence * Hq + query head
 template <int D>
 __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
     __shared__ __align__(16) PfLds<D> s;
@@ -284,7 +309,7 @@ __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
     const int bq = blockIdx.z, b = bq / p.Hq, hq = bq % p.Hq;
     const int h = hq / (p.Hq / p.Hkv);
     const int bh = b * p.Hkv + h;
-    const int qp = qtile * (QPW * 4) + wave * QPW + (lane & 31);   // this lane's query position
+    const int qp = qtile * QT + wave * QPW + (lane & 31);   // this lane's query position
     const bool qvalid = qp < p.P;
 
     PfState<D> w;
@@ -310,7 +335,11 @@ __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
         segg[k] = cnt * gpc;
         total += segg[k];
     }
-    const int g0 = (int)((long long)split * total / p.NS), g1 = (int)((long long)(split + 1) * total / p.NS);
+    // work list: the cached group blocks, then the new chunk's 32-token blocks;
+    // every split takes an equal share of both
+    const int nblk = (p.P + 31) / 32;
+    const int W = total + nblk;
+    const int g0 = (int)((long long)split * W / p.NS), g1 = (int)((long long)(split + 1) * W / p.NS);
     {
         int base = 0;
         pf_segment<D, 16>(w, s, p.pool[0] + (size_t)bh * p.cap[0] * gpc * group_bytes(16, D),
@@ -323,14 +352,14 @@ __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
                          max(g0 - base, 0), min(g1 - base, segg[2]), p.qscale, qp, p.P);
     }
 
-    // ---------------- the new chunk's own tokens (last split), causal
-    if (split == p.NS - 1) {
-        const int nblk = (p.P + 31) / 32;
+    // ---------------- this split's blocks of the new chunk's own tokens, causal
+    {
         // blocks past this tile's last query see nothing
-        const int last = min(nblk, (qtile * QPW * 4 + QPW * 4 + 31) / 32);
+        const int last = min(nblk, (qtile * QT + QT + 31) / 32);
+        const int nb0 = max(g0 - total, 0), nb1 = min(g1 - total, last);
         const uint16_t* kn = p.k_new + (size_t)bh * p.P * D;
         const uint16_t* vn = p.v_new + (size_t)bh * p.P * D;
-        for (int nb = 0; nb < last; ++nb) {
+        for (int nb = nb0; nb < nb1; ++nb) {
             __syncthreads();
             for (int c = tid; c < 32 * S; c += PT) {
                 const int t = c / S, L = c % S, tp = 32 * nb + t;
@@ -339,16 +368,19 @@ __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
                     ku = *reinterpret_cast<const uint4*>(kn + (size_t)tp * D + 8 * L);
                     vu = *reinterpret_cast<const uint4*>(vn + (size_t)tp * D + 8 * L);
                 }
-                *reinterpret_cast<uint4*>(&s.k[t][8 * L]) = ku;
+                *reinterpret_cast<uint4*>(&s.tile[0].k[t][8 * L]) = ku;
                 const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    s.vt[8 * L + 2 * e][t] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] & 0xffffu));
-                    s.vt[8 * L + 2 * e + 1][t] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] >> 16));
+                    const int c0 = 8 * L + 2 * e, c1 = c0 + 1;
+                    s.tile[0].vt[c0][4 * ((t >> 2) ^ vt_swz(c0)) + (t & 3)] =
+                        __builtin_bit_cast(_Float16, (uint16_t)(vw[e] & 0xffffu));
+                    s.tile[0].vt[c1][4 * ((t >> 2) ^ vt_swz(c1)) + (t & 3)] =
+                        __builtin_bit_cast(_Float16, (uint16_t)(vw[e] >> 16));
                 }
             }
             __syncthreads();
-            pf_block<D>(w, s, p.qscale, true, 32 * nb, qp, p.P);
+            pf_block<D>(w, s.tile[0], p.qscale, true, 32 * nb, qp, p.P);
         }
     }
 
@@ -397,7 +429,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillParams p) {
 }
 
 hipError_t launch_prefill(const PrefillParams& pp, int D, hipStream_t st) {
-    const dim3 grid((pp.P + QPW * 4 - 1) / (QPW * 4), pp.NS, pp.B * pp.Hq);
+    const dim3 grid((pp.P + QT - 1) / QT, pp.NS, pp.B * pp.Hq);
     const size_t rows = (size_t)pp.B * pp.Hq * pp.P;
     const dim3 cgrid((unsigned)((rows + 3) / 4));
     if (D == 128) {
