@@ -92,11 +92,13 @@ constexpr int kAttnGranule = 512;
 // Largest whole-cache cost, in granules, that the split handles.
 constexpr long long kAttnMaxGranules = (1LL << 31) - 1;
 // Cost of a unit per byte, in sixteenths, for segment k (FP16, INT4, INT2)
-// and hb query heads per KV head: the workgroup time per byte measured on
-// each segment relative to INT4.  With one head per KV head the kernel
-// streams at the same rate on every segment; with grouped-query heads the
-// arithmetic per byte counts (an INT2 byte holds twice the codes of an INT4
-// byte, an FP16 byte needs no unpacking).  Equal-cost ranges finish together.
+// and hb query heads per KV head: the workgroup time per byte on each
+// segment relative to INT4, fitted from per-workgroup timings with four heads
+// per KV head (with two, halfway between one and four).  With one head per
+// KV head the kernel streams at the same rate on every segment; with
+// grouped-query heads the arithmetic per byte counts (an INT2 byte holds
+// twice the codes of an INT4 byte, an FP16 byte needs no unpacking).
+// Equal-cost ranges finish together.
 constexpr int attn_cost16(int hb, int k) {
     return hb == 1 ? 16
          : hb == 2 ? (k == 0 ? 11 : k == 1 ? 16 : 22)
