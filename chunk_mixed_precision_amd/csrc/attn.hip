@@ -79,7 +79,14 @@ __device__ __forceinline__ float row_max(float v) {
     return v;
 }
 
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// Packed codes are read once per call: nontemporal loads (the `nt` bit) keep
+// them from displacing reusable lines and stream measurably faster than
+// plain loads on this part.
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
+    const u32x4_nt x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
 __device__ __forceinline__ float4 ldf4(const uint8_t* p) { return *reinterpret_cast<const float4*>(p); }
 
 __device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_cast(float4, u); }

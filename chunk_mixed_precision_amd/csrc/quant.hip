@@ -20,6 +20,17 @@
 
 namespace mkv {
 
+// Pool writes are streaming: every byte is written once and read back only by
+// later calls, so they go out as nontemporal stores (the `nt` bit), which
+// measured a few percent faster than plain stores here.
+template <class T>
+__device__ __forceinline__ void store_nt(uint8_t* p, T v) {
+    static_assert(sizeof(T) % 4 == 0, "whole dwords");
+    typedef uint32_t dwords __attribute__((ext_vector_type(sizeof(T) / 4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(dwords, v), reinterpret_cast<dwords*>(p));
+}
+
+
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -123,10 +134,10 @@ __global__ __launch_bounds__(64) void quant_pack_kernel(QuantParams p) {
         for (int i = 0; i < NL; ++i) {
             const int t = tr + TPI * i;
             const int kr = tok_of(S, ls, t);
-            *reinterpret_cast<u32x4*>(dst + ((size_t)kr * S + ls) * 16) = kcell[i];
+            store_nt(dst + ((size_t)kr * S + ls) * 16, kcell[i]);
             const int vr = ((t >> 2) << 2) | (ls & 3);
             const int vl = vslot_of(t & 3, ls >> 2, NG);
-            *reinterpret_cast<u32x4*>(dst + ((size_t)(vc_row0(16) + vr) * S + vl) * 16) = vcell[i];
+            store_nt(dst + ((size_t)(vc_row0(16) + vr) * S + vl) * 16, vcell[i]);
         }
         return;
     }
@@ -194,19 +205,19 @@ __global__ __launch_bounds__(64) void quant_pack_kernel(QuantParams p) {
                 word[c] = pack_word<BITS>(cf);
             }
             uint8_t* at = kcd + ((size_t)(2 * w + sub) * S + L) * 16 + e0 * 4;
-            if constexpr (CPL == 2) *reinterpret_cast<uint2*>(at) = make_uint2(word[0], word[1]);
-            else *reinterpret_cast<uint32_t*>(at) = word[0];
+            if constexpr (CPL == 2) store_nt(at, make_uint2(word[0], word[1]));
+            else store_nt(at, word[0]);
         }
         {   // key meta: rows 0/1 scales, rows 2/3 minima of channels 8L + 4 sub + e
             uint8_t* km = dst + (size_t)km_row0(BITS) * S * 16;
             uint8_t* as = km + ((size_t)sub * S + L) * 16 + e0 * 4;
             uint8_t* am = km + ((size_t)(2 + sub) * S + L) * 16 + e0 * 4;
             if constexpr (CPL == 2) {
-                *reinterpret_cast<float2*>(as) = make_float2(ks[0], ks[1]);
-                *reinterpret_cast<float2*>(am) = make_float2(kmn[0], kmn[1]);
+                store_nt(as, make_float2(ks[0], ks[1]));
+                store_nt(am, make_float2(kmn[0], kmn[1]));
             } else {
-                *reinterpret_cast<float*>(as) = ks[0];
-                *reinterpret_cast<float*>(am) = kmn[0];
+                store_nt(as, ks[0]);
+                store_nt(am, kmn[0]);
             }
         }
 
@@ -245,11 +256,11 @@ __global__ __launch_bounds__(64) void quant_pack_kernel(QuantParams p) {
             }
             const int m = t >> 2, Ls = vslot_of(t & 3, G, NG);
             if constexpr (BITS == 4) {
-                *reinterpret_cast<uint4*>(vcd + ((size_t)m * S + Ls) * 16) = make_uint4(words[0], words[1], words[2], words[3]);
+                store_nt(vcd + ((size_t)m * S + Ls) * 16, make_uint4(words[0], words[1], words[2], words[3]));
             } else {
-                *reinterpret_cast<uint2*>(vcd + ((size_t)(m >> 1) * S + Ls) * 16 + (m & 1) * 8) = make_uint2(words[0], words[1]);
+                store_nt(vcd + ((size_t)(m >> 1) * S + Ls) * 16 + (m & 1) * 8, make_uint2(words[0], words[1]));
             }
-            *reinterpret_cast<float2*>(vmd + ((size_t)(m >> 1) * S + Ls) * 16 + (m & 1) * 8) = make_float2(vs, vmn);
+            store_nt(vmd + ((size_t)(m >> 1) * S + Ls) * 16 + (m & 1) * 8, make_float2(vs, vmn));
         }
     };
     if (bits == 4) body(std::integral_constant<int, 4>{});

@@ -10,6 +10,8 @@
 
 namespace mkv {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 namespace {
 
 // bf16 -> float32 is exact: the bf16 bits are the high half of the float.
@@ -37,7 +39,11 @@ __global__ __launch_bounds__(256) void sim_partial_kernel(SimParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int tt = t + 4 * j;
-                u[j] = tt < p.C ? *reinterpret_cast<const uint4*>(xr + (size_t)tt * p.D) : make_uint4(0, 0, 0, 0);
+                u[j] = make_uint4(0, 0, 0, 0);
+                if (tt < p.C) {   // read once: nontemporal
+                    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + (size_t)tt * p.D));
+                    u[j] = make_uint4(x.x, x.y, x.z, x.w);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
