@@ -149,6 +149,8 @@ int mkv_route_chunks(const void* x_bf16, const void* w12_bf16, const float* w3, 
         if (logits && !aligned16(logits)) return MKV_ERR_ARG;
         if (D <= 0 || I <= 0) return MKV_ERR_ARG;
         if (D % 64 != 0 || I % mkv::kRouterBI != 0) return MKV_ERR_UNSUPPORTED;
+        // the GEMM addresses the 2I weight rows with 32-bit byte offsets
+        if ((size_t)2 * I * D * sizeof(uint16_t) > 0xFFFFFFFFull) return MKV_ERR_UNSUPPORTED;
         const size_t need = mkv_workspace_bytes(MKV_OP_ROUTE, B, T, D, I, 0, nullptr);
         if (!workspace || !aligned16(workspace) || workspace_bytes < need) return MKV_ERR_WORKSPACE;
         if ((long)B * T > 2147483647L) return MKV_ERR_UNSUPPORTED;

@@ -36,29 +36,30 @@ constexpr int LDA = BM + 1;            // epilogue: a[inner][token], padded row 
 constexpr int NSTAGE = kRouterStages;  // LDS ring depth
 constexpr int LDS_BYTES = (NSTAGE * STAGE > BI * LDA * 4) ? NSTAGE * STAGE : BI * LDA * 4;
 static_assert((CPR == 8 || CPR == 4) && BM == BN && BM * ROWB % (NT * 16) == 0, "router tile shape");
-static_assert(NSTAGE >= 2 && (NSTAGE - 2) * 2 * LPS < 64, "vmcnt range");
+static_assert(NSTAGE == 2, "the main loop alternates two LDS stages");
 
 // 16-byte chunk c of tile row r sits at chunk c ^ ((r / (256 / ROWB)) % CPR)
 // of its LDS row: the 16 rows that one 256-byte LDS cycle of a fragment
 // load serves then fall on 16 distinct bank groups.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r / (256 / ROWB)) & (CPR - 1)); }
 
-// s_waitcnt immediate waiting until at most n vector memory loads are
-// outstanding (gfx9 encoding: vmcnt [3:0] and [15:14]; the other counters
-// left at their maximum).
-constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediate: lgkmcnt(0), the other counters left at their maximum
+// (gfx9 encoding).
+constexpr int kWaitLgkm0 = 0xC07F;
 
 }  // namespace
 
 // Router GEMM with the gate and the W3 projection fused in the epilogue.
 // Workgroup tile: 256 tokens x 128 inner indices (the W1 and the W2 rows of
 // those indices), K staged 64 at a time through two LDS buffers filled by
-// direct global->LDS loads.  512 threads = 8 waves, two per SIMD so that
+// direct buffer->LDS loads.  512 threads = 8 waves, two per SIMD so that
 // one wave's LDS fragment reads overlap the other's MFMAs: wave (wm, wn)
 // owns tokens wm*128..+127 and inner wn*32..+31, i.e. 4 x 2 MFMA 32x32x16
-// bf16 blocks (h1 and h2 of the same inner indices).  Tiles are ordered so
-// that the eight inner tiles of a token tile run on one XCD and share its
-// L2.
+// bf16 blocks (h1 and h2 of the same inner indices).  Each wave keeps two
+// register sets of fragments: the LDS reads of the next 16-wide K step go
+// out before the MFMAs of the current one, and the wait for them comes
+// only at the start of the next step.  Tiles are ordered so that the eight
+// inner tiles of a token tile run on one XCD and share its L2.
 __global__ __launch_bounds__(NT, 2) void router_gemm_kernel(RouterParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
@@ -75,27 +76,35 @@ __global__ __launch_bounds__(NT, 2) void router_gemm_kernel(RouterParams p) {
     const int m0 = mt * BM, i0 = nt * BI;
     const int D = p.D;
 
-    // this thread's source rows for its direct loads: load j fills LDS bytes
-    // [(j * NT + tid) * 16, +16) of the A (and of the B) region
-    const uint16_t* a_src[LPS];
-    const uint16_t* b_src[LPS];
+    // Direct loads: load j of this thread fills LDS bytes [(j*NT + tid)*16,
+    // +16) of the A (and of the B) region of a stage.  Addresses are a
+    // wave-uniform base (the workgroup's first row, advanced by K) plus a
+    // 32-bit per-lane byte offset, so the loads take the scalar-base form.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint8_t* xbase = reinterpret_cast<const uint8_t*>(p.x + (size_t)m0 * D);
+    const uint8_t* wbase = reinterpret_cast<const uint8_t*>(p.w12 + (size_t)i0 * D);
+    uint32_t a_off[LPS], b_off[LPS];
 #pragma unroll
     for (int j = 0; j < LPS; ++j) {
         const int r = (j * NT + tid) / CPR;                  // tile row
         const int c = swz(r, tid % CPR);                     // logical chunk held by this slot
-        const int xr = min(m0 + r, p.M - 1);                 // rows past M read a valid row
-        a_src[j] = p.x + (size_t)xr * D + c * 8;
-        const int wr = r < BI ? i0 + r : p.I + i0 + (r - BI);
-        b_src[j] = p.w12 + (size_t)wr * D + c * 8;
+        const int xr = min(r, p.M - 1 - m0);                 // rows past M read a valid row
+        a_off[j] = (uint32_t)(xr * D + c * 8) * 2u;
+        const int wr = r < BI ? r : p.I + (r - BI);
+        b_off[j] = (uint32_t)(wr * D + c * 8) * 2u;
     }
+    // buffer resources over the workgroup's rows (no range limit: every
+    // offset is in bounds by construction)
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)xbase, (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, -1, 0x00020000);
     auto stage_load = [&](int buf, int k0) {
-        uint8_t* base = lds + (buf % NSTAGE) * STAGE;
+        uint8_t* base = lds + buf * STAGE + wave_u * 64 * 16;
+        const unsigned koff = (unsigned)k0 * 2u;
 #pragma unroll
         for (int j = 0; j < LPS; ++j) {
-            __builtin_amdgcn_global_load_lds((glob_void*)(a_src[j] + k0),
-                                             (lds_void*)(base + (j * NT + wave * 64) * 16), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glob_void*)(b_src[j] + k0),
-                                             (lds_void*)(base + BM * ROWB + (j * NT + wave * 64) * 16), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)(base + j * NT * 16), 16, a_off[j], koff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void*)(base + BM * ROWB + j * NT * 16), 16, b_off[j],
+                                                     koff, 0, 0);
         }
     };
 
@@ -109,45 +118,61 @@ __global__ __launch_bounds__(NT, 2) void router_gemm_kernel(RouterParams p) {
 
     const int lr = lane & 31, lh = lane >> 5;
     const int nk = D / BK;
-    // Ring of NSTAGE LDS stages: stage s lives in buffer s % NSTAGE and is
-    // issued NSTAGE-1 iterations before it is read, into the buffer whose
-    // reads ended at the previous barrier.  A lane's loads complete in issue
-    // order, so "stage kt+1 has landed" is a bound on the loads issued after
-    // it; the barrier then makes every lane's part visible.
-    for (int st = 0; st < NSTAGE - 1 && st < nk; ++st) stage_load(st, st * BK);
-    if (nk > NSTAGE - 2) __builtin_amdgcn_s_waitcnt(wait_vm((NSTAGE - 2) * 2 * LPS));
-    else __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt % NSTAGE;
-        if (kt + NSTAGE - 1 < nk) stage_load(kt + NSTAGE - 1, (kt + NSTAGE - 1) * BK);
-        const uint8_t* As = lds + cur * STAGE;
+    // fragments of K step ks of the stage in buffer buf
+    auto load_frags = [&](bf16x8* af, bf16x8* bfr, int buf, int ks) {
+        const uint8_t* As = lds + buf * STAGE;
         const uint8_t* Bs = As + BM * ROWB;
+        const int c = 2 * ks + lh;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int r = wm * 128 + mb * 32 + lr;
+            af[mb] = *reinterpret_cast<const bf16x8*>(As + r * ROWB + swz(r, c) * 16);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int r = nb * BI + wn * 32 + lr;
+            bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + r * ROWB + swz(r, c) * 16);
+        }
+    };
+    // Two LDS stages.  Stage kt+1 is issued (after the barrier of step
+    // kt-1's last K step) into the buffer that stage kt-1 left, and awaited
+    // before the last K step of stage kt.  Fragments are double-buffered in
+    // registers: the reads of the next K step (the first of the next stage,
+    // after the barrier) go out before the MFMAs of the current one.
+    bf16x8 af[2][4], bfr[2][2];
+    stage_load(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (nk > 1) stage_load(1, BK);
+    load_frags(af[0], bfr[0], 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            const int c = 2 * ks + lh;
-            bf16x8 af[4], bfr[2];
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const int r = wm * 128 + mb * 32 + lr;
-                af[mb] = *reinterpret_cast<const bf16x8*>(As + r * ROWB + swz(r, c) * 16);
+            const int f = ks & 1;
+            // this step's fragments (read during the previous step's MFMAs)
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < BK / 16) {
+                load_frags(af[f ^ 1], bfr[f ^ 1], cur, ks + 1);
+            } else if (kt + 1 < nk) {
+                // every lane's part of stage kt+1 has landed and every wave
+                // has finished reading stage kt: its buffer takes stage kt+2
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (kt + 2 < nk) stage_load(cur, (kt + 2) * BK);
+                load_frags(af[f ^ 1], bfr[f ^ 1], cur ^ 1, 0);
             }
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int r = nb * BI + wn * 32 + lr;
-                bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + r * ROWB + swz(r, c) * 16);
-            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][mb], bfr[f][nb], acc[mb][nb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // loads issued after stage kt+1: those of stages kt+2 .. min(kt+NSTAGE-1, nk-1)
-        if (kt + NSTAGE - 1 < nk) __builtin_amdgcn_s_waitcnt(wait_vm((NSTAGE - 2) * 2 * LPS));
-        else __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---------------- epilogue: a = SiLU(h1 * h2) = u * sigmoid(u) into LDS as
     // a[inner][token], then this tile's share of z = a W3^T: thread (half,

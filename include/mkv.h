@@ -170,7 +170,7 @@ typedef struct mkv_cache {
  *   workspace  device scratch of at least
  *              mkv_workspace_bytes(MKV_OP_ROUTE, B, T, D, I, ...) bytes.
  * Limits: T % C == 0, C % 32 == 0, 32 <= C <= 1024; D % 64 == 0;
- *         I % 128 == 0 (router mode).
+ *         I % 128 == 0 and 2*I*D*2 bytes of W12 < 4 GiB (router mode).
  * ---------------------------------------------------------------------- */
 int mkv_route_chunks(const void* x_bf16, const void* w12_bf16,
                      const float* w3, const float* b3, float* logits,
