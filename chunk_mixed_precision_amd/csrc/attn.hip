@@ -51,6 +51,23 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each row of
+// 16 lanes (row shifts fill with 0), then lane 15 of rows 0 and 2 is added
+// to rows 1 and 3 and lane 31 to rows 2 and 3 (row broadcasts).  Every lane
+// must be active.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return x;
+}
+
+// Sum over the 64 lanes, wave-uniform.
+__device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_incl_sum(x), 63); }
+
 template <int B>
 __device__ __forceinline__ float cvt_ub(uint32_t x) {
     float r;
@@ -232,11 +249,9 @@ __device__ __forceinline__ int total_cost(const AttnParams& p) {
             su.init(p, b);
             x = su.cost;
         }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
-        t += x;
+        t += wave_sum(x);
     }
-    return __builtin_amdgcn_readfirstlane(t * p.Hkv);
+    return t * p.Hkv;
 }
 
 // Workgroups actually used: at most G, and few enough that every range is at
@@ -277,11 +292,9 @@ __device__ __forceinline__ int seq_offset(const AttnParams& p, int b) {
             su.init(p, bb);
             x = su.cost;
         }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
-        t += x;
+        t += wave_sum(x);
     }
-    return __builtin_amdgcn_readfirstlane(t * p.Hkv);
+    return t * p.Hkv;
 }
 
 // The sequence whose streams contain global offset x (x < total), and the
@@ -298,20 +311,14 @@ __device__ __forceinline__ int seq_containing(const AttnParams& p, int x, int& s
             su.init(p, b);
             v = su.cost * p.Hkv;
         }
-        // inclusive prefix over the lanes
-        int incl = v;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off);
-            if (lane >= off) incl += y;
-        }
+        const int incl = wave_incl_sum(v);
         const unsigned long long hit = __ballot(b < p.B && carry + incl > x);
         if (hit) {
             const int l = __builtin_ctzll(hit);
-            seq_off = __builtin_amdgcn_readfirstlane(carry + __shfl(incl - v, l));
+            seq_off = carry + __builtin_amdgcn_readlane(incl - v, l);
             return b0 + l;
         }
-        carry = __builtin_amdgcn_readfirstlane(carry + __shfl(incl, 63));
+        carry += __builtin_amdgcn_readlane(incl, 63);
     }
     seq_off = carry;
     return p.B;
@@ -886,13 +893,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
             sl.init_counts(p, cnt[0], cnt[1], cnt[2]);
             v = sl.cost * p.Hkv;
         }
-        incl = v;
-#pragma unroll
-        for (int o2 = 1; o2 < 64; o2 <<= 1) {
-            const int y = __shfl_up(incl, o2);
-            if (lane >= o2) incl += y;
-        }
-        total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        incl = wave_incl_sum(v);
+        total = __builtin_amdgcn_readlane(incl, 63);
     } else {
         total = total_cost<D, HB>(p);
     }
@@ -906,10 +908,9 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
     if (p.B <= 64) {
         const unsigned long long hit = __ballot(lane < p.B && incl > lo);
         b = __builtin_ctzll(hit);
-        off = __builtin_amdgcn_readfirstlane(__shfl(incl - v, b));
-        su.init_counts(p, __builtin_amdgcn_readfirstlane(__shfl(cnt[0], b)),
-                       __builtin_amdgcn_readfirstlane(__shfl(cnt[1], b)),
-                       __builtin_amdgcn_readfirstlane(__shfl(cnt[2], b)));
+        off = __builtin_amdgcn_readlane(incl - v, b);
+        su.init_counts(p, __builtin_amdgcn_readlane(cnt[0], b), __builtin_amdgcn_readlane(cnt[1], b),
+                       __builtin_amdgcn_readlane(cnt[2], b));
     } else {
         b = seq_containing<D, HB>(p, lo, off);
         if (b >= p.B) return;

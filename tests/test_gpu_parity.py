@@ -148,6 +148,26 @@ def test_mixed_chunks_exhaustive(d, C, Hq, Hkv, B, T):
     full_check(w, tab, cache, out, k, v, q, w.n, tk, tv)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,d", [(130, 2, 2, 64), (97, 4, 2, 128)])
+def test_more_than_64_sequences(B, Hq, Hkv, d):
+    """Batches past one wavefront of sequences: the attention split then
+    scans the sequences 64 at a time to find each range's first stream, and
+    the combine finds each stream's offset the same way."""
+    C, T = 128, 512
+    w = configs.Workload(name=f"wide-B{B}-{Hq}x{Hkv}-d{d}", seed=5 + B, B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, C=C,
+                         mix=(0.3, 0.4, 0.3), outlier_cols=2, outlier_mult=8.0)
+    note(f"wide batch {w.name}")
+    experts = synth.drawn_chunk_experts(w)
+    tab = build_tables_from_experts(experts, C, freeze=True)
+    k, v = synth.kv(w, DEV)
+    q = synth.query(w, DEV)
+    cache, out, tk, tv = run_quant_attn(w, tab, k, v, q, w.n, tail=3)
+    bits, rank, perm, seg = tables_np(tab)
+    P.check_reorder_only(bits, rank, perm, seg, w.n)
+    check_canary(cache, seg)
+    full_check(w, tab, cache, out, k, v, q, w.n, tk, tv)
+
+
 def test_without_routing_sharing_per_layer_tables():
     """The ablation without routing sharing (MoQAE, Key designs: RS off):
     every block routes its own hidden states with its own router, so every
