@@ -203,16 +203,14 @@ int mkv_select_chunks_by_similarity(const void* x_bf16, const void* qe_bf16, int
     sp.x = static_cast<const uint16_t*>(x_bf16);
     sp.qe = static_cast<const uint16_t*>(qe_bf16);
     sp.part = static_cast<float4*>(workspace);
-    sp.sim = sim;
-    sp.chunk_bits = tab->chunk_bits;
-    sp.B = B; sp.T = T; sp.D = D; sp.C = C; sp.n_max = tab->n_max; sp.chunk_offset = chunk_offset;
+    sp.B = B; sp.T = T; sp.D = D; sp.C = C;
     sp.ds = (D + mkv::kSimSlice - 1) / mkv::kSimSlice;
-    sp.tau_hi = tau_hi; sp.tau_lo = tau_lo;
-    sp.freeze_first = (flags & MKV_FREEZE_FIRST) ? 1 : 0;
     int s = hip_status(mkv::launch_similarity(sp, st));
     if (s) return s;
     mkv::ReorderParams op{tab->chunk_bits, tab->chunk_rank, tab->perm, tab->seg_count,
-                          chunk_offset + n_new, tab->n_max, nullptr};
+                          chunk_offset + n_new, tab->n_max, nullptr, {}};
+    op.sel = mkv::SelectStep{sp.part, sim, tab->chunk_bits, chunk_offset, n_new, sp.ds, tau_hi, tau_lo,
+                             (flags & MKV_FREEZE_FIRST) ? 1 : 0};
     return hip_status(mkv::launch_reorder(op, B, st));
 }
 

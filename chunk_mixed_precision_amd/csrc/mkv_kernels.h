@@ -34,6 +34,17 @@ struct VoteParams {
     int freeze_first;
 };
 
+// Optional first step of the reorder: chunk bitwidths from the similarity
+// partials (sel_part == nullptr: the bitwidths are already in the table).
+struct SelectStep {
+    const float4* sel_part; // [B][n_new][ds] partials of sim_partial_kernel
+    float* sim;             // [B][n_new] out, optional
+    uint8_t* chunk_bits;    // the table's bitwidths (written for the new chunks)
+    int first, n_new, ds;   // new chunks first .. first + n_new - 1
+    float tau_hi, tau_lo;
+    int freeze_first;
+};
+
 struct ReorderParams {
     const uint8_t* chunk_bits;
     int32_t* chunk_rank;
@@ -41,6 +52,7 @@ struct ReorderParams {
     int32_t* seg_count;
     int n_total, n_max;
     int32_t* bad;           // optional: set when a chunk's bitwidth is invalid
+    SelectStep sel;
 };
 
 // ---------------------------------------------------------------- similarity selection
@@ -50,11 +62,7 @@ struct SimParams {
     const uint16_t* x;      // [B][T][D] bf16 embeddings of the new chunks' tokens
     const uint16_t* qe;     // [B][D] bf16 query embeddings
     float4* part;           // [B][n_new][ds]: (q.S, |S|^2, |q|^2, 0) per dim slice
-    float* sim;             // [B][n_new] out, optional
-    uint8_t* chunk_bits;    // [B][n_max]
-    int B, T, D, C, n_max, chunk_offset, ds;
-    float tau_hi, tau_lo;
-    int freeze_first;
+    int B, T, D, C, ds;
 };
 
 // ---------------------------------------------------------------- chunked prefill

@@ -271,6 +271,31 @@ __global__ __launch_bounds__(256) void reorder_kernel(ReorderParams p) {
     const int per = (n + 255) / 256;
     const int c0 = min(tid * per, n), c1 = min(c0 + per, n);
     const uint8_t* bits = p.chunk_bits + (size_t)b * p.n_max;
+    if (p.sel.sel_part) {
+        // Similarity selection of the new chunks in this thread's share (the
+        // thread reads back only bitwidths it wrote itself): the slices'
+        // sums in slice order, the cosine in fp32 (0 when either vector is
+        // zero), FP16 at or above tau_hi, INT4 at or above tau_lo, INT2
+        // below; routing freezing pins chunk 0 to FP16.
+        const SelectStep& q = p.sel;
+        for (int c = max(c0, q.first); c < min(c1, q.first + q.n_new); ++c) {
+            const int cn = c - q.first;
+            float dot = 0.f, ss = 0.f, qq = 0.f;
+            const float4* pp = q.sel_part + ((size_t)b * q.n_new + cn) * q.ds;
+            for (int s = 0; s < q.ds; ++s) {
+                const float4 v = pp[s];
+                dot += v.x;
+                ss += v.y;
+                qq += v.z;
+            }
+            const float den = sqrtf(ss) * sqrtf(qq);
+            const float sim = den > 0.f ? dot / den : 0.f;
+            int e = sim >= q.tau_hi ? 0 : (sim >= q.tau_lo ? 1 : 2);
+            if (q.freeze_first && c == 0) e = 0;
+            q.chunk_bits[(size_t)b * p.n_max + c] = (uint8_t)bits_of_expert(e);
+            if (q.sim) q.sim[(size_t)b * q.n_new + cn] = sim;
+        }
+    }
     int local[3] = {0, 0, 0};
     for (int c = c0; c < c1; ++c) {
         int k = expert_of_bits(bits[c]);

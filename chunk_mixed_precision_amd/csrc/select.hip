@@ -4,7 +4,8 @@
 // tokens' embeddings -- the direction of their mean -- and scored by its
 // cosine with the query embedding; two thresholds map the score to FP16,
 // INT4 or INT2.  The work is one streaming read of the embeddings (HBM
-// bound); the bitwidths then go through the same reorder as the router's.
+// bound).  The thresholds are applied by the reorder kernel's first step,
+// which then reorders the chunks exactly as after routing.
 #include "mkv_internal.h"
 #include "mkv_kernels.h"
 
@@ -91,34 +92,9 @@ __global__ __launch_bounds__(256) void sim_partial_kernel(SimParams p) {
     }
 }
 
-// One thread per (new chunk, sequence): the slices' sums in slice order, the
-// cosine in fp32 (0 when either vector is zero), the thresholds (FP16 at or
-// above tau_hi, INT4 at or above tau_lo, INT2 below) and routing freezing.
-__global__ __launch_bounds__(256) void sim_select_kernel(SimParams p) {
-    const int n_new = p.T / p.C;
-    const int c = blockIdx.x * blockDim.x + threadIdx.x, b = blockIdx.y;
-    if (c >= n_new) return;
-    float dot = 0.f, ss = 0.f, qq = 0.f;
-    const float4* pp = p.part + ((size_t)b * n_new + c) * p.ds;
-    for (int s = 0; s < p.ds; ++s) {
-        const float4 v = pp[s];
-        dot += v.x;
-        ss += v.y;
-        qq += v.z;
-    }
-    const float den = sqrtf(ss) * sqrtf(qq);
-    const float sim = den > 0.f ? dot / den : 0.f;
-    int e = sim >= p.tau_hi ? 0 : (sim >= p.tau_lo ? 1 : 2);
-    const int chunk = p.chunk_offset + c;
-    if (p.freeze_first && chunk == 0) e = 0;
-    p.chunk_bits[(size_t)b * p.n_max + chunk] = (uint8_t)bits_of_expert(e);
-    if (p.sim) p.sim[(size_t)b * n_new + c] = sim;
-}
-
 hipError_t launch_similarity(const SimParams& sp, hipStream_t st) {
     const int n_new = sp.T / sp.C;
     sim_partial_kernel<<<dim3(sp.ds, n_new, sp.B), 256, 0, st>>>(sp);
-    sim_select_kernel<<<dim3((n_new + 255) / 256, sp.B), 256, 0, st>>>(sp);
     return hipGetLastError();
 }
 
