@@ -59,8 +59,10 @@ struct PfTile {
                                            // c ^ vt_swz(ch), spreading the writes over the banks
 };
 
-// Chunk swizzle of the value tile: the channel's 32-channel group.
-__device__ __forceinline__ constexpr int vt_swz(int ch) { return (ch >> 5) & 7; }
+// Chunk swizzle of the value tile: from the channel's 32-channel group g,
+// (g & 1) | 2 (g & 2) -- it never flips bit 1 of a chunk index, so chunks c
+// and c + 2, which one MFMA operand takes together, keep their order.
+__device__ __forceinline__ constexpr int vt_swz(int ch) { return ((ch >> 5) & 1) | (((ch >> 5) & 2) << 1); }
 
 template <int D>
 struct PfLds {
@@ -73,6 +75,33 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
 }
 __device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
+
+// Two fp16 results packed in one word: low = fp16(ya.h * wa + oa), high =
+// fp16(yb.h * wb + ob), where .h is the low (HSEL 0) or high (HSEL 1) fp16
+// half of ya / yb, and the products and sums are formed in fp32
+// (v_fma_mixlo_f16 / v_fma_mixhi_f16).
+// f(integral_constant<int, 0>{}), ..., f(integral_constant<int, N-1>{})
+template <int N, int I = 0, class Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+    if constexpr (I < N) {
+        fn(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(fn);
+    }
+}
+
+template <int HSEL>
+__device__ __forceinline__ uint32_t mix_pair(uint32_t ya, uint32_t yb, float wa, float oa, float wb, float ob) {
+    uint32_t d;
+    if constexpr (HSEL == 0)
+        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixhi_f16 %0, %4, %5, %6 op_sel_hi:[1,0,0]"
+            : "=&v"(d) : "v"(ya), "v"(wa), "v"(oa), "v"(yb), "v"(wb), "v"(ob));
+    else
+        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixhi_f16 %0, %4, %5, %6 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+            : "=&v"(d) : "v"(ya), "v"(wa), "v"(oa), "v"(yb), "v"(wb), "v"(ob));
+    return d;
+}
 
 // Packed group block (raw, 16-byte cells as laid out in the pool) -> fp16
 // keys and values in LDS.  Every thread writes whole 8-byte runs: four
@@ -114,59 +143,132 @@ __device__ __forceinline__ void dequant_block(PfTile<D>& s, const u32x4* raw) {
             }
         }
     } else {
+        // A code c placed at bits 4-5 / 4-7 (weight 16) or 6-7 (weight 64) of
+        // an fp16 half whose other bits are 0x6400 is the half 1024 + 16c (or
+        // 1024 + 64c).  With w = s/16 (s/64) and o = mn - 64s (mn - 16s) one
+        // mixed fma gives c*s + mn, rounded once to fp16 straight into the
+        // low or high half of the output word.  (o carries one fp32 rounding
+        // of at most 2^-24 * 64|s|, far below the fp16 rounding of the tile.)
         constexpr int F = 32 / BITS;            // codes per word
-        constexpr uint32_t MASK = (1u << BITS) - 1u;
-        constexpr int NP = F / 4;               // 4-token parts of a key word
-        const float* kmeta = reinterpret_cast<const float*>(&raw[km_row0(BITS) * S]);
-        // keys: item (code row, slot L, part p): channels 8L + 4(row&1) .. +3 of
-        // the 4 tokens held by fields 4p .. 4p+3 of word row>>1
-        for (int c = tid; c < kc_rows(BITS) * S * NP; c += PT) {
-            const int p = c % NP, L = (c / NP) % S, row = c / (NP * S);
+        // magic halves of word x: INT4 y[k] holds fields k (low half) and
+        // k + 4 (high half) at bits 4-7; INT2 y[2k] holds fields 2k, 2k + 8 at
+        // bits 4-5 and y[2k+1] fields 2k+1, 2k+9 at bits 6-7
+        // (the magic constant sits in a register so that mask-and-insert is
+        // one v_and_or_b32: a VOP3 takes no literal operand on this target)
+        uint32_t vmagic;
+        asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(vmagic));
+        auto magic = [vmagic](uint32_t x, uint32_t* y) {
+            const uint32_t src[4] = {x << 4, x, x >> 4, x >> 8};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (BITS == 4) {
+                    y[k] = (src[k] & 0x00F000F0u) | vmagic;
+                } else {
+                    y[2 * k] = (src[k] & 0x00300030u) | vmagic;
+                    y[2 * k + 1] = (src[k] & 0x00C000C0u) | vmagic;
+                }
+            }
+        };
+        // field f of a word: its magic register and half, and whether its
+        // weight is the 64 one
+        // (reg_of, half_of and wide_of are compile-time for every field below)
+        auto reg_of = [](int f) { return BITS == 4 ? (f & 3) : (f & 7); };
+        auto wide_of = [](int f) { return BITS == 2 && (f & 1); };
+        // one output word from channel/token words a and b (fields f)
+        auto pair_out = [&](auto f_tag, const uint32_t* ya, const uint32_t* yb, float wna, float ona, float wwa,
+                            float owa, float wnb, float onb, float wwb, float owb) {
+            constexpr int f = decltype(f_tag)::value;
+            constexpr int HS = BITS == 4 ? (f >> 2) : (f >> 3);
+            return wide_of(f) ? mix_pair<HS>(ya[reg_of(f)], yb[reg_of(f)], wwa, owa, wwb, owb)
+                              : mix_pair<HS>(ya[reg_of(f)], yb[reg_of(f)], wna, ona, wnb, onb);
+        };
+
+        constexpr int KH = BITS == 4 ? 1 : 2;   // key items per code cell (fields split in halves)
+        constexpr int NK = kc_rows(BITS) * S * KH;
+        constexpr int NW = 32 / F;              // value words per token and group
+        constexpr int VH = BITS == 4 ? 1 : 2;   // value items per word (channels split in halves)
+        constexpr int NV = 8 * NG * NW * VH;
+        constexpr int FPI = F / KH;             // fields per item (8)
+        static_assert(NK % 64 == 0 && NV % 64 == 0 && NK + NV <= PT, "one item per thread, wave-uniform kinds");
+        static_assert(F / KH == 8 && F / VH == 8, "eight fields per item");
+        if (tid < NK) {
+            // keys: cell (code row, slot L) = channels 8L + 4(row&1) .. +3; its
+            // word row>>1 holds field positions F*(row>>1) .. of each channel;
+            // this item takes fields FPI*kh .. +FPI-1
+            const int L = tid % S, row = (tid / S) % kc_rows(BITS), kh = tid / (S * kc_rows(BITS));
             const int w = row >> 1, j0 = 4 * (row & 1);
             const u32x4 u = raw[(kc_row0(BITS) + row) * S + L];
+            const float* kmeta = reinterpret_cast<const float*>(&raw[km_row0(BITS) * S]);
             const float4 sc = *reinterpret_cast<const float4*>(kmeta + ((row & 1) * S + L) * 4);
             const float4 mn = *reinterpret_cast<const float4*>(kmeta + ((2 + (row & 1)) * S + L) * 4);
+            const float scs[4] = {sc.x, sc.y, sc.z, sc.w}, mns[4] = {mn.x, mn.y, mn.z, mn.w};
+            float wn[4], on[4], ww[4], ow[4];
 #pragma unroll
-            for (int i = 4 * p; i < 4 * p + 4; ++i) {
-                const int t = tok_of(S, L, F * w + i);
-                const int sh = BITS * i;
-                const float x0 = __builtin_fmaf((float)((u[0] >> sh) & MASK), sc.x, mn.x);
-                const float x1 = __builtin_fmaf((float)((u[1] >> sh) & MASK), sc.y, mn.y);
-                const float x2 = __builtin_fmaf((float)((u[2] >> sh) & MASK), sc.z, mn.z);
-                const float x3 = __builtin_fmaf((float)((u[3] >> sh) & MASK), sc.w, mn.w);
-                *reinterpret_cast<uint2*>(&s.k[t][8 * L + j0]) = make_uint2(pack_h2(x0, x1), pack_h2(x2, x3));
+            for (int c = 0; c < 4; ++c) {
+                wn[c] = scs[c] * 0.0625f;
+                on[c] = __builtin_fmaf(-64.f, scs[c], mns[c]);
+                ww[c] = scs[c] * 0.015625f;
+                ow[c] = __builtin_fmaf(-16.f, scs[c], mns[c]);
             }
-        }
-        // values: item (token index mm, G, word u, channel quad h): channels
-        // 32G + F*u + 4h .. +3 of tokens 4mm .. 4mm+3 (token mm of slots tq*NG + G)
-        const float* vmeta = reinterpret_cast<const float*>(&raw[vm_row0(BITS) * S]);
-        constexpr int NW = 32 / F;              // words per token and group
-        constexpr int NH = F / 4;               // channel quads per word
-        for (int c = tid; c < 8 * NG * NW * NH; c += PT) {
-            const int mm = c & 7, G = (c >> 3) % NG, u = (c / (8 * NG)) % NW, h = c / (8 * NG * NW);
+            uint32_t y[4][8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) magic(u[c], y[c]);
+            // token of field position F*w + f: the xor of f into that of F*w
+            // (f < 16 touches only the bits that tok_of permutes)
+            const int t0 = tok_of(S, L, F * w);
+            _Float16* krow = &s.k[0][8 * L + j0];
+            auto fields = [&](auto kh_tag) {
+                constexpr int KHV = decltype(kh_tag)::value;
+                static_for<FPI>([&](auto i_tag) {
+                    constexpr int f = FPI * KHV + decltype(i_tag)::value;
+                    static_assert(f < 16, "field inside its 16-token half");
+                    const int t = t0 ^ f;
+                    const uint32_t o0 = pair_out(std::integral_constant<int, f>{}, y[0], y[1], wn[0], on[0], ww[0],
+                                                 ow[0], wn[1], on[1], ww[1], ow[1]);
+                    const uint32_t o1 = pair_out(std::integral_constant<int, f>{}, y[2], y[3], wn[2], on[2], ww[2],
+                                                 ow[2], wn[3], on[3], ww[3], ow[3]);
+                    *reinterpret_cast<uint2*>(krow + t * (D + 8)) = make_uint2(o0, o1);
+                });
+            };
+            if (KH == 1 || kh == 0) fields(std::integral_constant<int, 0>{});
+            else fields(std::integral_constant<int, KH - 1>{});
+        } else if (tid < NK + NV) {
+            // values: item (token index mm, G, word u, channel half vh): the
+            // channels 32G + F*u + 8vh .. +7 of tokens 4mm .. 4mm+3 (token mm of
+            // the slots tq*NG + G)
+            const int c = tid - NK;
+            const int mm = c & 7, G = (c >> 3) % NG, u = (c / (8 * NG)) % NW, vh = c / (8 * NG * NW);
             const int row = BITS == 4 ? mm : (mm >> 1);
             const int dw = BITS == 4 ? u : 2 * (mm & 1) + u;
-            float sv[4], mv[4];
-            uint32_t wd[4];
+            const float* vmeta = reinterpret_cast<const float*>(&raw[vm_row0(BITS) * S]);
+            float wn[4], on[4], ww[4], ow[4];
+            uint32_t y[4][8];
 #pragma unroll
             for (int tq = 0; tq < 4; ++tq) {
-                const int L = tq * NG + G;
+                const int L = vslot_of(tq, G, NG);
                 const float2 sm = *reinterpret_cast<const float2*>(vmeta + ((mm >> 1) * S + L) * 4 + 2 * (mm & 1));
-                sv[tq] = sm.x;
-                mv[tq] = sm.y;
-                const u32x4 q4 = raw[(vc_row0(BITS) + row) * S + L];
-                wd[tq] = dw == 0 ? q4[0] : (dw == 1 ? q4[1] : (dw == 2 ? q4[2] : q4[3]));
+                wn[tq] = sm.x * 0.0625f;
+                on[tq] = __builtin_fmaf(-64.f, sm.x, sm.y);
+                ww[tq] = sm.x * 0.015625f;
+                ow[tq] = __builtin_fmaf(-16.f, sm.x, sm.y);
+                magic(reinterpret_cast<const uint32_t*>(&raw[(vc_row0(BITS) + row) * S + L])[dw], y[tq]);
             }
-            const int ch = 32 * G + F * u + 4 * h;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sh = BITS * (4 * h + j);
-                float x[4];
-#pragma unroll
-                for (int tq = 0; tq < 4; ++tq) x[tq] = __builtin_fmaf((float)((wd[tq] >> sh) & MASK), sv[tq], mv[tq]);
-                *reinterpret_cast<uint2*>(&s.vt[ch + j][4 * (mm ^ vt_swz(ch + j))]) =
-                    make_uint2(pack_h2(x[0], x[1]), pack_h2(x[2], x[3]));
-            }
+            const int ch0 = 32 * G + F * u + 8 * vh;
+            const int col = 4 * (mm ^ vt_swz(ch0));     // the same for the item's 8 channels (one group)
+            auto channels = [&](auto vh_tag) {
+                constexpr int VHV = decltype(vh_tag)::value;
+                static_for<8>([&](auto i_tag) {
+                    constexpr int i = decltype(i_tag)::value;
+                    constexpr int f = 8 * VHV + i;
+                    const uint32_t o0 = pair_out(std::integral_constant<int, f>{}, y[0], y[1], wn[0], on[0], ww[0],
+                                                 ow[0], wn[1], on[1], ww[1], ow[1]);
+                    const uint32_t o1 = pair_out(std::integral_constant<int, f>{}, y[2], y[3], wn[2], on[2], ww[2],
+                                                 ow[2], wn[3], on[3], ww[3], ow[3]);
+                    *reinterpret_cast<uint2*>(&s.vt[ch0 + i][col]) = make_uint2(o0, o1);
+                });
+            };
+            if (VH == 1 || vh == 0) channels(std::integral_constant<int, 0>{});
+            else channels(std::integral_constant<int, VH - 1>{});
         }
     }
 }
@@ -215,11 +317,14 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, floa
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * qscale;
     const float mn = fmaxf(w.m, mloc);
     const float alpha = (mn == -INFINITY) ? 1.f : exp2_fast(w.m - mn);
+    // a lane with no visible token yet (mn = -inf) has only -inf scores,
+    // which the reference 0 sends to exp2(-inf) = 0
+    const float mref = (mn == -INFINITY) ? 0.f : mn;
     float ps = 0.f;
     f16x8 pf0, pf1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const float pr = (mn == -INFINITY) ? 0.f : exp2_fast(__builtin_fmaf(st[r], qscale, -mn));
+        const float pr = exp2_fast(__builtin_fmaf(st[r], qscale, -mref));
         ps += pr;
         if (r < 8) pf0[r] = (_Float16)pr;
         else pf1[r - 8] = (_Float16)pr;
@@ -240,9 +345,9 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, floa
         // tokens of accumulator registers 8ks2 .. 8ks2+7 of this lane
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
-            // chunks 4ks2 + lh and 4ks2 + 2 + lh of channel 32t + lr (swizzle t)
-            const f16x4 v0 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][4 * ((4 * ks2 + lh) ^ (t & 7))]);
-            const f16x4 v1 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][4 * ((4 * ks2 + 2 + lh) ^ (t & 7))]);
+            // chunks 4ks2 + lh and 4ks2 + 2 + lh of channel 32t + lr (swizzled)
+            const f16x4 v0 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][4 * ((4 * ks2 + lh) ^ vt_swz(32 * t))]);
+            const f16x4 v1 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][4 * ((4 * ks2 + 2 + lh) ^ vt_swz(32 * t))]);
             const f16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             w.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ks2 ? pf1 : pf0, w.o[t], 0, 0, 0);
         }
