@@ -51,18 +51,41 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The value of lane l ^ 32.  v_permlane32_swap exchanges the upper half of
+// one register with the lower half of another; applied to two copies of x,
+// lanes 0-31 of the second copy and lanes 32-63 of the first then hold the
+// other half's values.  (Written out: the compiler builtin folded a max of
+// its two results to the first one.)  The s_nop covers the VALU write of
+// the copies ahead of the permute.
+__device__ __forceinline__ float swap_halves(float x) {
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    const bool upper = (threadIdx.x & 32) != 0;
+    return __builtin_bit_cast(float, upper ? a : b);
+}
+
+// Value tile geometry: channel-major rows of 32 tokens + 4 pad (72 bytes),
+// 32 rows per 32-channel group, and 16 more bytes after every group, so that
+// group g starts 4g banks further on: the dequant writes of one row of
+// lanes (four groups x four 8-channel words) fall on distinct banks.
+constexpr int VT_ROW = 36;                        // halves per channel row
+constexpr int VT_GROUP = 32 * VT_ROW + 8;         // halves per 32-channel group
+
 template <int D>
 struct PfTile {
     _Float16 k[32][D + 8];                 // keys of a block, token-major (rows padded by 16 bytes)
-    _Float16 vt[D][36];                    // values, channel-major: 32 tokens + 4 pad (72-byte rows);
-                                           // the 4-token chunk c of channel ch sits at chunk
-                                           // c ^ vt_swz(ch), spreading the writes over the banks
+    _Float16 vt[D / 32][VT_GROUP];         // values, channel-major (see VT_ROW / VT_GROUP)
 };
 
-// Chunk swizzle of the value tile: from the channel's 32-channel group g,
-// (g & 1) | 2 (g & 2) -- it never flips bit 1 of a chunk index, so chunks c
-// and c + 2, which one MFMA operand takes together, keep their order.
-__device__ __forceinline__ constexpr int vt_swz(int ch) { return ((ch >> 5) & 1) | (((ch >> 5) & 2) << 1); }
+// Token chunk c (tokens 4c .. 4c+3) of channel ch in the value tile.
+template <int D>
+__device__ __forceinline__ _Float16* vt_at(PfTile<D>& s, int ch, int c) {
+    return &s.vt[ch >> 5][(ch & 31) * VT_ROW + 4 * c];
+}
+template <int D>
+__device__ __forceinline__ const _Float16* vt_at(const PfTile<D>& s, int ch, int c) {
+    return &s.vt[ch >> 5][(ch & 31) * VT_ROW + 4 * c];
+}
 
 template <int D>
 struct PfLds {
@@ -138,7 +161,7 @@ __device__ __forceinline__ void dequant_block(PfTile<D>& s, const u32x4* raw) {
                 const uint32_t a1 = (j & 1) ? hi16(w[1][wi]) : lo16(w[1][wi]);
                 const uint32_t a2 = (j & 1) ? hi16(w[2][wi]) : lo16(w[2][wi]);
                 const uint32_t a3 = (j & 1) ? hi16(w[3][wi]) : lo16(w[3][wi]);
-                *reinterpret_cast<uint2*>(&s.vt[ch + j][4 * (m ^ vt_swz(ch + j))]) =
+                *reinterpret_cast<uint2*>(vt_at(s, ch + j, m)) =
                     make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
             }
         }
@@ -237,7 +260,10 @@ __device__ __forceinline__ void dequant_block(PfTile<D>& s, const u32x4* raw) {
             // channels 32G + F*u + 8vh .. +7 of tokens 4mm .. 4mm+3 (token mm of
             // the slots tq*NG + G)
             const int c = tid - NK;
-            const int mm = c & 7, G = (c >> 3) % NG, u = (c / (8 * NG)) % NW, vh = c / (8 * NG * NW);
+            // lanes next to each other take other groups and words of the same
+            // token quad: their raw words and their tile rows both spread
+            // over the banks
+            const int G = c % NG, u = (c / NG) % NW, vh = (c / (NG * NW)) % VH, mm = c / (NG * NW * VH);
             const int row = BITS == 4 ? mm : (mm >> 1);
             const int dw = BITS == 4 ? u : 2 * (mm & 1) + u;
             const float* vmeta = reinterpret_cast<const float*>(&raw[vm_row0(BITS) * S]);
@@ -254,7 +280,6 @@ __device__ __forceinline__ void dequant_block(PfTile<D>& s, const u32x4* raw) {
                 magic(reinterpret_cast<const uint32_t*>(&raw[(vc_row0(BITS) + row) * S + L])[dw], y[tq]);
             }
             const int ch0 = 32 * G + F * u + 8 * vh;
-            const int col = 4 * (mm ^ vt_swz(ch0));     // the same for the item's 8 channels (one group)
             auto channels = [&](auto vh_tag) {
                 constexpr int VHV = decltype(vh_tag)::value;
                 static_for<8>([&](auto i_tag) {
@@ -264,7 +289,7 @@ __device__ __forceinline__ void dequant_block(PfTile<D>& s, const u32x4* raw) {
                                                  ow[0], wn[1], on[1], ww[1], ow[1]);
                     const uint32_t o1 = pair_out(std::integral_constant<int, f>{}, y[2], y[3], wn[2], on[2], ww[2],
                                                  ow[2], wn[3], on[3], ww[3], ow[3]);
-                    *reinterpret_cast<uint2*>(&s.vt[ch0 + i][col]) = make_uint2(o0, o1);
+                    *reinterpret_cast<uint2*>(vt_at(s, ch0 + i, mm)) = make_uint2(o0, o1);
                 });
             };
             if (VH == 1 || vh == 0) channels(std::integral_constant<int, 0>{});
@@ -293,14 +318,29 @@ template <int D>
 __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, float qscale, bool causal, int base,
                                          int qp, int P) {
     const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
+    // every fragment read of the block goes out first: the key fragments,
+    // then the value fragments (K step ks2 of tile t covers tokens 16ks2 +
+    // 8(j>>2) + 4lh + (j&3), j = 0..7 -- the tokens of accumulator registers
+    // 8ks2 .. 8ks2+7 of this lane -- i.e. chunks 4ks2 + lh and 4ks2 + 2 + lh
+    // of channel 32t + lr), whose latency the scores and the softmax hide
+    f16x8 kf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = *reinterpret_cast<const f16x8*>(&s.k[lr][16 * ks + 8 * lh]);
+    __builtin_amdgcn_sched_barrier(0);
+    f16x8 vf[D / 32][2];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+            const f16x4 v0 = *reinterpret_cast<const f16x4*>(vt_at(s, 32 * t + lr, 4 * ks2 + lh));
+            const f16x4 v1 = *reinterpret_cast<const f16x4*>(vt_at(s, 32 * t + lr, 4 * ks2 + 2 + lh));
+            vf[t][ks2] = f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        }
     f32x16 st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(&s.k[lr][16 * ks + 8 * lh]);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w.qf[ks], st, 0, 0, 0);
-    }
+    for (int ks = 0; ks < D / 16; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], w.qf[ks], st, 0, 0, 0);
     // st[r]: token 8(r>>2) + 4lh + (r&3) of the block, query qp
     // raw scores; the scale (> 0) is applied inside the exponent's fma
     float mloc = -INFINITY;
@@ -314,7 +354,7 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, floa
         st[r] = x;
         mloc = fmaxf(mloc, x);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * qscale;
+    mloc = fmaxf(mloc, swap_halves(mloc)) * qscale;     // with the query's other tokens
     const float mn = fmaxf(w.m, mloc);
     const float alpha = (mn == -INFINITY) ? 1.f : exp2_fast(w.m - mn);
     // a lane with no visible token yet (mn = -inf) has only -inf scores,
@@ -340,18 +380,10 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, floa
             for (int r = 0; r < 16; ++r) w.o[t][r] *= alpha;
     }
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-        // K step ks2 covers tokens 16ks2 + 8(j>>2) + 4lh + (j&3), j = 0..7: the
-        // tokens of accumulator registers 8ks2 .. 8ks2+7 of this lane
+    for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-            // chunks 4ks2 + lh and 4ks2 + 2 + lh of channel 32t + lr (swizzled)
-            const f16x4 v0 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][4 * ((4 * ks2 + lh) ^ vt_swz(32 * t))]);
-            const f16x4 v1 = *reinterpret_cast<const f16x4*>(&s.vt[32 * t + lr][4 * ((4 * ks2 + 2 + lh) ^ vt_swz(32 * t))]);
-            const f16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            w.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ks2 ? pf1 : pf0, w.o[t], 0, 0, 0);
-        }
-    }
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+            w.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[t][ks2], ks2 ? pf1 : pf0, w.o[t], 0, 0, 0);
 }
 
 // Group blocks [lo, hi) of one bitwidth segment.  Raw blocks stream into a
@@ -478,10 +510,8 @@ __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int c0 = 8 * L + 2 * e, c1 = c0 + 1;
-                    s.tile[0].vt[c0][4 * ((t >> 2) ^ vt_swz(c0)) + (t & 3)] =
-                        __builtin_bit_cast(_Float16, (uint16_t)(vw[e] & 0xffffu));
-                    s.tile[0].vt[c1][4 * ((t >> 2) ^ vt_swz(c1)) + (t & 3)] =
-                        __builtin_bit_cast(_Float16, (uint16_t)(vw[e] >> 16));
+                    vt_at(s.tile[0], c0, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] & 0xffffu));
+                    vt_at(s.tile[0], c1, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] >> 16));
                 }
             }
             __syncthreads();
