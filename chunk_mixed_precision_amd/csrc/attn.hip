@@ -741,9 +741,9 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     // ---- unit loop.  Every phase's loads are issued one phase ahead, into
     // the other of two 8-row register buffers; the last phase of a unit
     // prefetches the first phase of the next unit this wavefront holds a
-    // ticket for (or, when there is none, re-reads its own: a cache hit that
-    // keeps the loop free of a branch whose merge point would make the
-    // compiler wait for every outstanding load).  Tickets are taken in
+    // ticket for (or, when there is none, a stand-in read of this unit's
+    // first bytes, which keeps the loop free of a branch whose merge point
+    // would make the compiler wait for every outstanding load).  Tickets are taken in
     // increasing order, so a wavefront meets the segments in the order FP16,
     // INT4, INT2 and the three loops below run once each.
     auto run_unit = [&](auto bits_tag, auto par_tag, const uint8_t* ub, uint32_t vo, const uint8_t* ubn,
@@ -763,11 +763,13 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     };
 
     // one step: process unit U (whose first phase is in the buffer of parity
-    // PAR) and move to the next ticket; with no next unit the prefetch
-    // re-reads this one
+    // PAR) and move to the next ticket; with no next unit the prefetch reads
+    // the first 16 bytes of this unit's rows with every lane (one cache line
+    // per load instead of the unit's phase: the codes are loaded
+    // nontemporally, so a re-read of the phase would go back to HBM)
     auto step = [&](auto bits_tag, auto par_tag, int k, int segg_k, int ubase_k) {
         const int Un = grab();
-        uint32_t von = vo;
+        uint32_t von = 0;
         const uint8_t* ubn = ub;
         if (Un < U1) ubn = unit_addr(Un, von);
         const bool valid = (U - ubase_k) * GPI + gslot < segg_k;
