@@ -92,6 +92,8 @@ def test_route_argument_errors():
     assert route(D=100) == E.MKV_ERR_UNSUPPORTED
     assert route(I=100) == E.MKV_ERR_UNSUPPORTED
     assert route(I=192) == E.MKV_ERR_UNSUPPORTED
+    assert route(D=65536, I=16384) == E.MKV_ERR_UNSUPPORTED       # W12 of 4 GiB: past 32-bit offsets
+    assert route(D=65536, I=16256) == E.MKV_ERR_WORKSPACE         # just under: only the workspace is missing
     assert route(x=0x101) == E.MKV_ERR_ARG                       # misaligned
     assert route(off=1) == E.MKV_ERR_ARG                         # offset without MKV_APPEND
     assert route(tab=_tables(n_max=1)) == E.MKV_ERR_ARG          # 2 chunks > n_max
