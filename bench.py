@@ -370,6 +370,21 @@ def main():
                "effective_gbs": round(pre_bytes / t_pre / 1e9, 1), "bytes_per_launch": pre_bytes}
         del pq, pkn, pvn, pout, pws
 
+    # a plain device-to-device copy on the same box, for scale: bytes read + written per second
+    cp_bytes = 512 << 20
+    csrc = torch.ones(cp_bytes, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    ev_cp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in ev_cp:
+        a.record()
+        cdst.copy_(csrc)
+        b.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * cp_bytes / (float(np.median([a.elapsed_time(b) for a, b in ev_cp])) * 1e-3) / 1e9
+    del csrc, cdst
+
     t_pack = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
     t_route = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
     t_attn = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(nev)]) * 1e-3
@@ -407,6 +422,8 @@ def main():
                      "kernel": "mkv_mixed_kv_decode_attention call (attn_tile_kernel + attn_combine_kernel)",
                      "bytes_per_launch": attn_bytes, "avg_launch_us": round(a_mean * 1e6, 3)},
         "quantize_tokens_per_s": round(w.B * w.T / float(t_pack.mean()), 1),
+        "device_copy": {"gbs": round(copy_gbs, 1), "bytes_moved": 2 * cp_bytes,
+                        "attention_frac_of_copy": round(attn_gbs / copy_gbs, 4)},
         "kernels": {
             "route": {"us": round(float(t_route.mean()) * 1e6, 2),
                       "roofline": {"bound": "mfma", "achieved": round(router_flop / float(t_route.mean()) / 1e12, 2),
