@@ -299,14 +299,17 @@ def main():
     nev = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nev)]
 
+    # one step in the order of the data flow: route and vote, quantize/pack with that routing,
+    # then decode attention.  Attention reads the cache copy written R - 1 steps earlier, so the
+    # bytes quantize has just written cannot serve it from the last-level cache.
     def step(i, rec):
         e = ev[i] if rec else None
         if e:
             e[0].record()
-        mkv.quantize_pack_kv(k, v, tab, caches[i % R])
+        mkv.route_chunks(tab, w.C, x=x, w12=w12, w3=w3, b3=b3, workspace=ws_route)
         if e:
             e[1].record()
-        mkv.route_chunks(tab, w.C, x=x, w12=w12, w3=w3, b3=b3, workspace=ws_route)
+        mkv.quantize_pack_kv(k, v, tab, caches[i % R])
         if e:
             e[2].record()
         mkv.mixed_kv_decode_attention(q, caches[(i + 1) % R], out=out, workspace=ws_attn)
@@ -385,8 +388,8 @@ def main():
     copy_gbs = 2 * cp_bytes / (float(np.median([a.elapsed_time(b) for a, b in ev_cp])) * 1e-3) / 1e9
     del csrc, cdst
 
-    t_pack = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
-    t_route = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
+    t_route = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
+    t_pack = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
     t_attn = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(nev)]) * 1e-3
 
     attn_bytes = configs.effective_attention_bytes(w, seg)

@@ -944,6 +944,14 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
 // between, at records (b*Hkv + h) + w.  512 threads: thread (tgi, qd) owns
 // channel quad qd and merges pieces tgi, tgi + TGR, ... online, with its
 // loads batched so that they are in flight together.
+//
+// Finding the pieces takes a load of the segment counts and the split
+// arithmetic, and the records can only be loaded after that.  When the
+// streams have equal cost (one sequence, or sequences of equal mix) the first
+// owner of stream bh is floor(bh*G/(B*Hkv)) up to rounding, so every thread
+// first loads its share of the TGR records from one below that guess on;
+// when the true pieces lie inside that window (the common case) the merge
+// uses them and waits for one round of loads instead of two.
 template <int D, int HB>
 __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
     constexpr int NT = 512;
@@ -957,6 +965,19 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv, h = bh % p.Hkv;
     const int tid = threadIdx.x, qd = tid % QPR, tgi = tid / QPR;
+    const int nslots = p.B * p.Hkv + p.G;   // records in the workspace (per query head of the group)
+    const int wg = max(0, (int)(((long long)bh * p.G) / (p.B * p.Hkv)) - 1);
+    float2 sml[HB];
+    float4 sov[HB];
+    {
+        const int slot = min(bh + wg + tgi, nslots - 1);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const float* rec = p.part + ((size_t)slot * HB + hb) * (D + 4);
+            sml[hb] = *reinterpret_cast<const float2*>(rec + D);
+            sov[hb] = *reinterpret_cast<const float4*>(rec + 4 * qd);
+        }
+    }
     if (tid < 64) {
         int w0 = 0, np = 0;
         const int total = total_cost<D, HB>(p);
@@ -978,9 +999,11 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
     }
     __syncthreads();
     const int w0 = s_range[0], npiece = s_range[1];
+    const bool spec = w0 >= wg && w0 + npiece <= wg + TGR;   // all pieces inside the loaded window
     auto rec_of = [&](int v, int hb) {
         return p.part + ((size_t)(bh + w0 + v) * HB + hb) * (D + 4);
     };
+#pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
         const int hq = h * HB + hb;
         if (p.tail_len > 0) {
@@ -997,7 +1020,14 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
         }
         float m = -INFINITY, l = 0.f;
         float o[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int v0 = tgi; v0 < npiece; v0 += TGR * BATCH) {
+        if (spec) {
+            // piece wg + tgi - w0 (a valid piece's slot is always below nslots)
+            const int v = wg + tgi - w0;
+            if (v >= 0 && v < npiece) {
+                const float o2[4] = {sov[hb].x, sov[hb].y, sov[hb].z, sov[hb].w};
+                merge_run<4>(m, l, o, sml[hb].x, sml[hb].y, o2);
+            }
+        } else for (int v0 = tgi; v0 < npiece; v0 += TGR * BATCH) {
             float2 ml[BATCH];
             float4 ov[BATCH];
 #pragma unroll
