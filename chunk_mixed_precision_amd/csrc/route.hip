@@ -219,13 +219,18 @@ __global__ __launch_bounds__(NT, 2) void router_gemm_kernel(RouterParams p) {
     }
 }
 
-// One block of 256 threads per (new chunk, sequence).
+// One block of 256 threads per (new chunk, sequence).  Each wavefront counts
+// its tokens' experts with ballots and popcounts, the four wavefronts' counts
+// meet in LDS, and the chunk takes the expert with the most tokens (the
+// smallest index on a tie).
 __global__ __launch_bounds__(256) void vote_kernel(VoteParams p) {
-    __shared__ int cnt[3];
+    __shared__ int wcnt[4][3];            // per-wavefront expert counts
     const int c = blockIdx.x, b = blockIdx.y;
-    if (threadIdx.x < 3) cnt[threadIdx.x] = 0;
-    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int M = p.B * p.T;
+    // counts of this wavefront's tokens, wave-uniform (ballot + popcount;
+    // a lane past the chunk end takes no part in the ballots)
+    int n_all = 0, n1 = 0, n2 = 0;
     for (int t = threadIdx.x; t < p.C; t += blockDim.x) {
         const size_t row = (size_t)b * p.T + (size_t)c * p.C + t;
         float z[3];
@@ -249,10 +254,20 @@ __global__ __launch_bounds__(256) void vote_kernel(VoteParams p) {
         if (z[1] > best) { e = 1; best = z[1]; }
         if (z[2] > best) { e = 2; }
         if (p.token_expert) p.token_expert[row] = (uint8_t)e;
-        atomicAdd(&cnt[e], 1);
+        n_all += __popcll(__ballot(1));
+        n1 += __popcll(__ballot(e == 1));
+        n2 += __popcll(__ballot(e == 2));
+    }
+    if (lane == 0) {
+        wcnt[wave][0] = n_all - n1 - n2;
+        wcnt[wave][1] = n1;
+        wcnt[wave][2] = n2;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
+        int cnt[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) cnt[k] = (wcnt[0][k] + wcnt[1][k]) + (wcnt[2][k] + wcnt[3][k]);
         int v = 0;
         if (cnt[1] > cnt[v]) v = 1;
         if (cnt[2] > cnt[v]) v = 2;
