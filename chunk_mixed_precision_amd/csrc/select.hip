@@ -23,9 +23,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // One workgroup of 4 wavefronts per (512-dim slice, new chunk, sequence).
 // Lane l holds dims 8l..8l+7 of the slice; wavefront w sums tokens w, w+4,
-// ... of the chunk with four 16-byte loads in flight per lane.  The four
-// wavefronts' sums meet in LDS (added in wavefront order), and wavefront 0
-// reduces q.S, |S|^2 and |q|^2 over the slice.
+// ... of the chunk with two 16-byte loads in flight per lane (four or more
+// made the whole read slower on this part).  The four wavefronts' sums meet
+// in LDS (added in wavefront order), and wavefront 0 reduces q.S, |S|^2 and
+// |q|^2 over the slice.
 __global__ __launch_bounds__(256) void sim_partial_kernel(SimParams p) {
     __shared__ float4 red[4][2][64];
     const int slice = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
@@ -35,10 +36,10 @@ __global__ __launch_bounds__(256) void sim_partial_kernel(SimParams p) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (act) {
         const uint16_t* xr = p.x + ((size_t)b * p.T + (size_t)c * p.C) * p.D + d0;
-        for (int t = wave; t < p.C; t += 16) {
-            uint4 u[4];
+        for (int t = wave; t < p.C; t += 8) {
+            uint4 u[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
                 const int tt = t + 4 * j;
                 u[j] = make_uint4(0, 0, 0, 0);
                 if (tt < p.C) {   // read once: nontemporal
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(256) void sim_partial_kernel(SimParams p) {
                 }
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
                 const uint32_t w4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
