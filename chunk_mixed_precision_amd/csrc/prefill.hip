@@ -535,6 +535,10 @@ __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
 
 // One wavefront per (sequence, query head, query): the splits' records merged
 // with the log-sum-exp combine; lane l owns channels (D/64)*l .. +D/64-1.
+// Lane sp first loads split sp's (m, l) (at most 32 splits), so the maximum,
+// the weights and the denominator come from one round of loads and wave
+// reductions; the splits' channel values are then loaded in batches of
+// eight, independent of each other.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillParams p) {
     const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -542,19 +546,40 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillParams p) {
     const size_t rows = (size_t)p.B * p.Hq * p.P;
     if (row >= rows) return;
     constexpr int PL = D / 64;                 // channels per lane
+    constexpr int BATCH = 8;
     const float* recs = p.part + row * p.NS * (D + 4);
-    float M = -INFINITY;
-    for (int sp = 0; sp < p.NS; ++sp) M = fmaxf(M, recs[(size_t)sp * (D + 4) + D]);
-    float acc[PL] = {}, L = 0.f;
-    if (M != -INFINITY) {
-        for (int sp = 0; sp < p.NS; ++sp) {
-            const float* r = recs + (size_t)sp * (D + 4);
-            const float ms = r[D];
-            if (ms == -INFINITY) continue;
-            const float wgt = exp2_fast(ms - M);
-            L = __builtin_fmaf(r[D + 1], wgt, L);
+    float ms = -INFINITY, ls = 0.f;
+    if (lane < p.NS) {
+        const float2 ml = *reinterpret_cast<const float2*>(recs + (size_t)lane * (D + 4) + D);
+        ms = ml.x;
+        ls = ml.y;
+    }
+    float M = ms;
 #pragma unroll
-            for (int c = 0; c < PL; ++c) acc[c] = __builtin_fmaf(r[PL * lane + c], wgt, acc[c]);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    // weight of split `lane` (0 for a split that saw no token, and for all
+    // of them when no split did)
+    const float wl = (ms == -INFINITY) ? 0.f : exp2_fast(ms - M);
+    float L = ls * wl;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    float acc[PL] = {};
+    for (int s0 = 0; s0 < p.NS; s0 += BATCH) {
+        float v[BATCH][PL];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int sp = min(s0 + j, p.NS - 1);
+            const float* r = recs + (size_t)sp * (D + 4) + PL * lane;
+#pragma unroll
+            for (int c = 0; c < PL; ++c) v[j][c] = r[c];
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            if (s0 + j >= p.NS) break;
+            const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s0 + j));
+            if (wgt == 0.f) continue;
+#pragma unroll
+            for (int c = 0; c < PL; ++c) acc[c] = __builtin_fmaf(v[j][c], wgt, acc[c]);
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
