@@ -303,7 +303,8 @@ __global__ __launch_bounds__(256) void reorder_kernel(ReorderParams p) {
             const int cn = c - q.first;
             float dot = 0.f, ss = 0.f, qq = 0.f;
             const float4* pp = q.sel_part + ((size_t)b * q.n_new + cn) * q.ds;
-            for (int s = 0; s < q.ds; ++s) {
+#pragma unroll 8
+            for (int s = 0; s < q.ds; ++s) {   // in slice order; eight loads go out together
                 const float4 v = pp[s];
                 dot += v.x;
                 ss += v.y;
