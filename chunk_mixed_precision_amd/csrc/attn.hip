@@ -51,23 +51,6 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each row of
-// 16 lanes (row shifts fill with 0), then lane 15 of rows 0 and 2 is added
-// to rows 1 and 3 and lane 31 to rows 2 and 3 (row broadcasts).  Every lane
-// must be active.
-__device__ __forceinline__ int wave_incl_sum(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
-    return x;
-}
-
-// Sum over the 64 lanes, wave-uniform.
-__device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_incl_sum(x), 63); }
-
 template <int B>
 __device__ __forceinline__ float cvt_ub(uint32_t x) {
     float r;

@@ -284,9 +284,12 @@ __global__ __launch_bounds__(256) void vote_kernel(VoteParams p) {
 }
 
 // One block of 256 threads per sequence: stable partition of chunks
-// [0, n_total) into the FP16, INT4, INT2 segments.
+// [0, n_total) into the FP16, INT4, INT2 segments.  Thread t owns a
+// contiguous share of the chunks; its slot in each segment is the count of
+// that segment's chunks in the shares before it (a wavefront DPP scan plus
+// the four wavefronts' totals).
 __global__ __launch_bounds__(256) void reorder_kernel(ReorderParams p) {
-    __shared__ int pre[3][257];
+    __shared__ int wtot[4][3];            // per-wavefront segment counts
     const int b = blockIdx.x, tid = threadIdx.x;
     const int n = p.n_total;
     const int per = (n + 255) / 256;
@@ -327,24 +330,38 @@ __global__ __launch_bounds__(256) void reorder_kernel(ReorderParams p) {
         }
         ++local[k];
     }
+    // exclusive prefix of the counts in thread order: a DPP scan inside each
+    // wavefront, then the four wavefronts' totals through LDS
+    const int lane = tid & 63, wave = tid >> 6;
+    int incl[3];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) pre[k][tid + 1] = local[k];
-    if (tid == 0) {
-        pre[0][0] = pre[1][0] = pre[2][0] = 0;
+    for (int k = 0; k < 3; ++k) incl[k] = wave_incl_sum(local[k]);
+    if (lane == 63) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) wtot[wave][k] = incl[k];
     }
     __syncthreads();
-    if (tid < 3) {
-        for (int i = 1; i <= 256; ++i) pre[tid][i] += pre[tid][i - 1];
+    int excl[3], tot[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        int before = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int x = wtot[w][k];
+            before += w < wave ? x : 0;
+            all += x;
+        }
+        excl[k] = before + incl[k] - local[k];
+        tot[k] = all;
     }
-    __syncthreads();
-    const int tot0 = pre[0][256], tot1 = pre[1][256], tot2 = pre[2][256];
+    const int tot0 = tot[0], tot1 = tot[1], tot2 = tot[2];
     if (tid == 0) {
         p.seg_count[b * 3 + 0] = tot0;
         p.seg_count[b * 3 + 1] = tot1;
         p.seg_count[b * 3 + 2] = tot2;
     }
     const int start[3] = {0, tot0, tot0 + tot1};
-    int run[3] = {pre[0][tid], pre[1][tid], pre[2][tid]};
+    int run[3] = {excl[0], excl[1], excl[2]};
     for (int c = c0; c < c1; ++c) {
         int k = expert_of_bits(bits[c]);
         if (k < 0) k = 2;
