@@ -573,3 +573,163 @@ def test_pins_catch_planted_prefill_mistakes(mistake):
         o = f(q, np.zeros((0, d)), np.zeros((0, d)), kn, vn)
         assert np.allclose(o[0], vn[0], atol=0, rtol=0)
         assert np.allclose(o, orc.prefill_attention(q, np.zeros((0, d)), np.zeros((0, d)), kn, vn))
+
+
+# ---------------------------------------------------------------- dequantization and code placement
+# MoQAE notes, "Overall framework": each chunk's cache is stored at its
+# bitwidth and attention then runs as usual on the decoded values; "Related
+# work" (KIVI): keys are grouped per channel, values per token.  The chunks
+# below are built from chosen codes, scales and minima, so the decoded value
+# of every element is known exactly without running the oracle.
+def _lossless_key_chunk(bits, C=64, d=64, seed=0):
+    """Keys [C, d] built as code * s + mn with a distinct power-of-two s and a
+    distinct half-integer mn for every (32-token group, channel); each group
+    holds code 0 and code L, so min-max quantization recovers exactly these
+    codes, scales and minima (every product and sum is exact)."""
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(seed + bits)
+    G = C // 32
+    codes = rng.integers(0, L + 1, size=(C, d))
+    s = np.zeros((G, d))
+    mn = np.zeros((G, d))
+    for g in range(G):
+        for j in range(d):
+            s[g, j] = 2.0 ** -(1 + (g + 2 * j) % 4)
+            mn[g, j] = -0.5 * (1 + (5 * g + 3 * j) % 11)
+            t0, t1 = rng.choice(32, size=2, replace=False)
+            codes[32 * g + t0, j] = 0
+            codes[32 * g + t1, j] = L
+    x = np.zeros((C, d))
+    for t in range(C):
+        for j in range(d):
+            x[t, j] = codes[t, j] * s[t // 32, j] + mn[t // 32, j]
+    assert np.array_equal(x.astype(np.float16).astype(np.float64), x)
+    return x.astype(np.float16), codes, s, mn
+
+
+def _lossless_value_chunk(bits, C=64, d=64, seed=0):
+    """Values [C, d]: the same construction with one (s, mn) per (token,
+    32-channel group)."""
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(seed + 100 + bits)
+    NG = d // 32
+    codes = rng.integers(0, L + 1, size=(C, d))
+    s = np.zeros((C, NG))
+    mn = np.zeros((C, NG))
+    for t in range(C):
+        for g in range(NG):
+            s[t, g] = 2.0 ** -(1 + (t + 3 * g) % 4)
+            mn[t, g] = -0.5 * (1 + (7 * t + 2 * g) % 13)
+            j0, j1 = rng.choice(32, size=2, replace=False)
+            codes[t, 32 * g + j0] = 0
+            codes[t, 32 * g + j1] = L
+    x = np.zeros((C, d))
+    for t in range(C):
+        for j in range(d):
+            x[t, j] = codes[t, j] * s[t, j // 32] + mn[t, j // 32]
+    assert np.array_equal(x.astype(np.float16).astype(np.float64), x)
+    return x.astype(np.float16), codes, s, mn
+
+
+def check_dequant_hand_chunks(qk, qv, dk, dv):
+    """qk/qv: quantize_chunk_k/v; dk/dv: dequant_k/v (the functions under
+    test).  The decoded chunk must equal the constructed values element by
+    element, and quantization must return the constructed codes, scales and
+    minima at their own positions."""
+    for bits in (4, 2):
+        k, kc, ks, km = _lossless_key_chunk(bits)
+        assert np.array_equal(dk(kc.astype(np.uint8), ks.astype(np.float32), km.astype(np.float32)),
+                              k.astype(np.float64)), f"dequant_k INT{bits}"
+        q, s, mn = qk(k, bits)
+        assert np.array_equal(q, kc), f"key codes INT{bits}"
+        assert np.array_equal(s.astype(np.float64), ks) and np.array_equal(mn.astype(np.float64), km)
+        assert np.array_equal(dk(q, s, mn), k.astype(np.float64))
+        v, vc, vs, vm = _lossless_value_chunk(bits)
+        assert np.array_equal(dv(vc.astype(np.uint8), vs.astype(np.float32), vm.astype(np.float32)),
+                              v.astype(np.float64)), f"dequant_v INT{bits}"
+        q, s, mn = qv(v, bits)
+        assert np.array_equal(q, vc), f"value codes INT{bits}"
+        assert np.array_equal(s.astype(np.float64), vs) and np.array_equal(mn.astype(np.float64), vm)
+        assert np.array_equal(dv(q, s, mn), v.astype(np.float64))
+
+
+def test_dequant_hand_built_chunks():
+    check_dequant_hand_chunks(orc.quantize_chunk_k, orc.quantize_chunk_v, orc.dequant_k, orc.dequant_v)
+
+
+def _group_step(vals, bits):
+    """s of one group from its own extremes, evaluated in exact rationals
+    with float32 rounding (independent of numpy's float32)."""
+    xs = [Fraction(float(v)) for v in vals]
+    return float(fl32(fl32(max(xs) - min(xs)) / ((1 << bits) - 1)))
+
+
+def check_round_trip_bound(qk, qv, dk, dv, C=128, d=64):
+    """Random chunks with outlier key channels: every decoded element lies
+    within half a step (+4 float32 ulps of the group's range ends) of its
+    input, where the step is computed here from the element's own group:
+    keys, the 32 tokens of its channel in its 32-token block; values, the 32
+    channels of its token in its 32-channel block."""
+    rng = np.random.default_rng(99)
+    k = rng.standard_normal((C, d))
+    k[:, [1, 17, 40]] *= 10.0                          # outlier channels
+    k = k.astype(np.float16)
+    v = rng.standard_normal((C, d)).astype(np.float16)
+    for bits in (4, 2):
+        for x, which in ((k, "k"), (v, "v")):
+            q, s, mn = (qk if which == "k" else qv)(x, bits)
+            xh = (dk if which == "k" else dv)(q, s, mn)
+            xf = x.astype(np.float64)
+            bound = {}
+            for t in range(C):
+                for j in range(d):
+                    key = (t // 32, j) if which == "k" else (t, j // 32)
+                    if key not in bound:
+                        if which == "k":
+                            grp = xf[32 * (t // 32):32 * (t // 32) + 32, j]
+                        else:
+                            grp = xf[t, 32 * (j // 32):32 * (j // 32) + 32]
+                        ulp = float(np.spacing(np.float32(max(abs(grp.min()), abs(grp.max())))))
+                        bound[key] = _group_step(grp, bits) / 2 + 4 * ulp
+                    assert abs(xf[t, j] - xh[t, j]) <= bound[key], (which, bits, t, j)
+
+
+def test_round_trip_error_bound_per_element():
+    check_round_trip_bound(orc.quantize_chunk_k, orc.quantize_chunk_v, orc.dequant_k, orc.dequant_v)
+
+
+def _dequant_k_tiled(codes, scale, mn):
+    C, d = codes.shape
+    reps = (C // scale.shape[0], 1)
+    return codes.astype(np.float64) * np.tile(scale.astype(np.float64), reps) + np.tile(mn.astype(np.float64), reps)
+
+
+def _dequant_v_reversed_min(codes, scale, mn):
+    s = np.repeat(scale.astype(np.float64), 32, axis=1)
+    m = np.repeat(mn[:, ::-1].astype(np.float64), 32, axis=1)
+    return codes.astype(np.float64) * s + m
+
+
+def _quantize_k_no_transpose(k, bits):
+    C, d = k.shape
+    g = np.asarray(k).reshape(C // 32, 32, d).transpose(0, 2, 1)
+    q, s, mn = orc.quantize_groups(g, bits)
+    return q.reshape(C, d), s, mn
+
+
+@pytest.mark.parametrize("mistake", ["dequant_k_tile", "dequant_v_reversed_min", "quantize_k_no_transpose"])
+def test_pins_catch_planted_dequant_mistakes(mistake):
+    fns = dict(qk=orc.quantize_chunk_k, qv=orc.quantize_chunk_v, dk=orc.dequant_k, dv=orc.dequant_v)
+    if mistake == "dequant_k_tile":
+        fns["dk"] = _dequant_k_tiled
+    elif mistake == "dequant_v_reversed_min":
+        fns["dv"] = _dequant_v_reversed_min
+    else:
+        fns["qk"] = _quantize_k_no_transpose
+    caught = 0
+    for check in (check_dequant_hand_chunks, check_round_trip_bound):
+        try:
+            check(**fns)
+        except AssertionError:
+            caught += 1
+    assert caught == 2, f"{mistake} passed {2 - caught} of the two pins"
