@@ -192,3 +192,27 @@ def test_stream_helper_argument_errors():
     assert grow(0x1000, 0x100000, 8, 1, 2, 1, 2, 128, 128, None) == E.MKV_ERR_UNSUPPORTED
     assert grow(0x1000, 0x2000, 4, 1, 2, 1, 2, 128, 128, None) == E.MKV_ERR_ARG     # overlap
     assert grow(None, 0x100000, 4, 1, 2, 1, 2, 128, 128, None) == E.MKV_ERR_ARG
+
+
+def prefill(Hq=2, P=64, cache=None, q=0x600, kn=0x800, vn=0x900, out=0x700, ws=None, wsb=0):
+    cache = cache or _cache()
+    return mkv.lib().mkv_mixed_kv_prefill_attention(q, Hq, P, ctypes.byref(cache), kn, vn, out, ws, wsb, None)
+
+
+def test_prefill_argument_errors():
+    E = mkv
+    assert prefill(q=None) == E.MKV_ERR_ARG
+    assert prefill(kn=None) == E.MKV_ERR_ARG
+    assert prefill(vn=0x908) == E.MKV_ERR_ARG                   # misaligned
+    assert prefill(out=0x704) == E.MKV_ERR_ARG
+    assert prefill(Hq=3) == E.MKV_ERR_ARG                       # not a multiple of Hkv
+    assert prefill(P=0) == E.MKV_ERR_ARG
+    assert prefill(P=65536) == E.MKV_ERR_UNSUPPORTED
+    assert prefill(Hq=65536) == E.MKV_ERR_UNSUPPORTED           # B*Hq past the grid
+    assert prefill(cache=_cache(d=96)) == E.MKV_ERR_UNSUPPORTED
+    c = _cache()
+    c.seg_count = None
+    assert prefill(cache=c) == E.MKV_ERR_ARG
+    assert prefill() == E.MKV_ERR_WORKSPACE
+    assert prefill(ws=0x9000, wsb=64) == E.MKV_ERR_WORKSPACE
+    assert mkv.workspace_bytes_prefill(1, 2, 64, 128, 128, [1, 1, 1]) > 0
