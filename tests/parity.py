@@ -24,6 +24,11 @@ from tests import layout_ref
 
 ATTN_TOL = 2e-3
 NEAR_TIE = 1e-4
+# Two attention calls on the same inputs differ only in the fp32 summation
+# order (work units are handed to wavefronts dynamically).  The measured
+# spread stays below about 1.1e-5 of max|o| per (sequence, head); this bound
+# leaves a few times that.
+RUN_TO_RUN = 5e-5
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

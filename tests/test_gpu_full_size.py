@@ -78,9 +78,26 @@ def test_llama2_7b_128k_layer():
     routed_single_layer(configs.LLAMA2_7B_128K, n_heads=2)
 
 
+class _SequenceView:
+    """One sequence of a packed cache, addressed as a cache of B = 1: the
+    pools are laid out [B][Hkv][cap][...], so sequence b's part of each pool
+    is one contiguous run of bytes."""
+
+    def __init__(self, cache, b):
+        self.B, self.Hkv, self.d, self.C, self.caps = 1, cache.Hkv, cache.d, cache.C, cache.caps
+        self.pools_np = []
+        for k, bits in enumerate(orc.EXPERT_BITS):
+            per = mkv.pool_bytes(bits, 1, cache.Hkv, cache.caps[k], cache.d, cache.C)
+            self.pools_np.append(P.to_np(cache.pools[k][b * per:(b + 1) * per]))
+
+
+@pytest.mark.timeout(900)
 def test_llama2_13b_40_layers_sampled():
-    """One routing table (drawn mix, routing sharing) for 40 layers; layers
-    0, 19 and 39 are built and checked on sequences 0, 7, 15."""
+    """One routing table (drawn mix, routing sharing) for 40 layers.  Every
+    query head of sequences 0, 7 and 15 in layers 0, 19 and 39, plus every
+    head of 5 seeded random (layer, sequence) pairs, is compared with the
+    oracle over all 8192 cached tokens; sampled chunks of every bitwidth are
+    compared bit for bit in each layer built."""
     w = configs.LLAMA2_13B_40L
     rng = np.random.default_rng(w.seed)
     experts = synth.drawn_chunk_experts(w)
@@ -92,21 +109,34 @@ def test_llama2_13b_40_layers_sampled():
     avg = float((seg * np.array([16, 4, 2])).sum() / seg.sum())
     note(f"{w.name}: mix {seg.sum(0).tolist()}, {avg:.3f} bits per value")
     caps = [int(seg[:, kk].max()) for kk in range(3)]
-    for layer in (0, 19, 39):
+    pairs = {layer: [0, 7, 15] for layer in (0, 19, 39)}
+    for _ in range(5):
+        layer, b = int(rng.integers(w.layers)), int(rng.integers(w.B))
+        pairs.setdefault(layer, [])
+        if b not in pairs[layer]:
+            pairs[layer].append(b)
+    note(f"  (layer, sequences) checked: {sorted(pairs.items())}")
+    for layer in sorted(pairs):
         k, v = synth.kv(w, DEV, layer=layer)
         q = synth.query(w, DEV, layer=layer)
         cache = mkv.PackedCache(w.B, w.Hkv, w.d, w.C, caps, tab.seg_count, DEV)
         mkv.quantize_pack_kv(k, v, tab, cache)
         out = mkv.mixed_kv_decode_attention(q, cache)
         torch.cuda.synchronize()
-        pools = P.pools_np(cache)
-        k_np, v_np = P.to_np(k), P.to_np(v)
-        triples = sample_chunks(rng, bits, w.B, w.Hkv, w.n, per_bits=4)
-        n = P.check_quantize(cache, pools, k_np, v_np, bits, rank, triples)
-        pairs = [(b, int(h)) for b in (0, 7, 15) for h in rng.choice(w.Hq, size=3, replace=False)]
-        err = P.check_attention(cache, pools, bits, rank, w.n, P.to_np(q), P.to_np(out), pairs)
-        note(f"  layer {layer}: {n} chunks exact, attention rel err {err:.2e} on {len(pairs)} heads")
-        del k, v, cache, pools, k_np, v_np
+        q_np, out_np = P.to_np(q), P.to_np(out)
+        n = 0
+        worst = 0.0
+        for b in pairs[layer]:
+            view = _SequenceView(cache, b)
+            triples = sample_chunks(rng, bits[b:b + 1], 1, w.Hkv, w.n, per_bits=2)
+            n += P.check_quantize(view, view.pools_np, P.to_np(k[b:b + 1]), P.to_np(v[b:b + 1]),
+                                  bits[b:b + 1], rank[b:b + 1], triples)
+            err = P.check_attention(view, view.pools_np, bits[b:b + 1], rank[b:b + 1], w.n, q_np[b:b + 1],
+                                    out_np[b:b + 1], [(0, hq) for hq in range(w.Hq)])
+            worst = max(worst, err)
+        note(f"  layer {layer}: sequences {pairs[layer]}, all {w.Hq} heads each: attention rel err {worst:.2e}; "
+             f"{n} chunks exact")
+        del k, v, cache, out
 
 
 def test_llama3_8b_gqa_append_step():

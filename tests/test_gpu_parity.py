@@ -304,8 +304,8 @@ def test_determinism():
     scale = o1.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
     rel = ((o1 - o2).abs() / scale).max().item()
     note(f"attention run-to-run max rel difference {rel:.2e}")
-    # two runs differ only in summation order; allow a tenth of the parity bar
-    assert rel <= P.ATTN_TOL / 10
+    # two runs differ only in summation order
+    assert rel <= P.RUN_TO_RUN
 
 
 def test_workspace_reuse_across_calls():
@@ -321,8 +321,9 @@ def test_workspace_reuse_across_calls():
     outs = [mkv.mixed_kv_decode_attention(q, cache, workspace=ws).clone() for _ in range(3)]
     torch.cuda.synchronize()
     scale = out.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
-    for o in outs:
-        assert ((o - out).abs() / scale).max().item() <= P.ATTN_TOL / 10
+    rels = [((o - out).abs() / scale).max().item() for o in outs]
+    note(f"attention repeated-call max rel differences {[f'{r:.2e}' for r in rels]}")
+    assert max(rels) <= P.RUN_TO_RUN
 
 
 def test_append_mode_tables():
