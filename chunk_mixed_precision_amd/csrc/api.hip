@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mkv.h"
 #include "mkv_internal.h"
 #include "mkv_kernels.h"
@@ -70,6 +72,95 @@ inline int check_cache_shape(const mkv_cache* c) {
     return MKV_OK;
 }
 
+
+// Decode attention: the argument checks shared by both entry points (no
+// launch, no HIP call).  Resolves a tail_stride of 0 to tail_len.
+int attention_args(const void* q_fp16, int Hq, const mkv_cache* cache, const void* tail_k_fp16,
+                   const void* tail_v_fp16, int tail_len, int* tail_stride, const float* out) {
+    if (!q_fp16 || !out || !aligned16(q_fp16) || !aligned16(out)) return MKV_ERR_ARG;
+    if (!valid_cache(cache)) return MKV_ERR_ARG;
+    int s = check_cache_shape(cache);
+    if (s) return s;
+    if (Hq <= 0 || Hq % cache->Hkv != 0) return MKV_ERR_ARG;
+    const int g = Hq / cache->Hkv;
+    if (g != 1 && g != 2 && g != 4) return MKV_ERR_UNSUPPORTED;
+    if ((long)cache->B * Hq > 2147483647L) return MKV_ERR_UNSUPPORTED;
+    if (tail_len < 0 || tail_len >= 4096) return MKV_ERR_ARG;
+    if (tail_len > 0 && (!tail_k_fp16 || !tail_v_fp16)) return MKV_ERR_ARG;
+    if (*tail_stride == 0) *tail_stride = tail_len;
+    if (*tail_stride < tail_len) return MKV_ERR_ARG;
+    {   // the work split counts the cost of the whole cache at capacity in 32-bit granules
+        const int gpi = (512 / cache->d) * mkv::attn_heads_per_row(g) / g;   // group blocks per unit
+        const int bits[3] = {16, 4, 2};
+        long long gran = 0;
+        for (int k = 0; k < 3; ++k) {
+            const long long units = ((long long)cache->cap[k] * (cache->C / mkv::kGroup) + gpi - 1) / gpi;
+            gran += units * ((long long)gpi * mkv::group_bytes(bits[k], cache->d) * mkv::attn_cost16(g, k) /
+                             (16 * mkv::kAttnGranule));
+        }
+        if (gran * cache->B * cache->Hkv > mkv::kAttnMaxGranules) return MKV_ERR_UNSUPPORTED;
+    }
+    return MKV_OK;
+}
+
+// Decode attention: the two launches (tile kernel, combine) on checked
+// arguments; `workspace` holds the tile partials of this call.
+int attention_launch(const void* q_fp16, int Hq, const mkv_cache* cache, const void* tail_k_fp16,
+                     const void* tail_v_fp16, int tail_len, int tail_stride, float* out, void* workspace,
+                     hipStream_t st) {
+    mkv::AttnParams ap{};
+    ap.q = static_cast<const uint16_t*>(q_fp16);
+    for (int k = 0; k < 3; ++k) {
+        ap.pool[k] = static_cast<const uint8_t*>(cache->pool[k]);
+        ap.cap[k] = cache->cap[k];
+    }
+    ap.seg_count = cache->seg_count;
+    ap.B = cache->B; ap.Hkv = cache->Hkv; ap.Hq = Hq; ap.C = cache->C;
+    ap.G = attn_workgroups(cache->B, cache->Hkv, cache->d, cache->cap, cache->C);
+    ap.part = static_cast<float*>(workspace);
+    ap.tail_k = static_cast<const uint16_t*>(tail_k_fp16);
+    ap.tail_v = static_cast<const uint16_t*>(tail_v_fp16);
+    ap.tail_len = tail_len;
+    ap.tail_stride = tail_stride;
+    ap.out = out;
+    ap.qscale = (float)(1.4426950408889634 / sqrt((double)cache->d));
+    return hip_status(mkv::launch_attention(ap, cache->d, Hq / cache->Hkv, st));
+}
+
+// ---- the no-allocation variant of decode attention ----------------------
+// Its tile partials live in `scratch`, a fixed device array that every GPU
+// the library runs on holds until the process ends.  In host code the
+// array's name is only a host-side stand-in, so kernels get the device
+// address that hipGetSymbolAddress reports, looked up once per device (with
+// that device current) on the first call there and kept per device.
+constexpr size_t kScratchBytes = MKV_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[MKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+int scratch_of_current_device(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return MKV_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return MKV_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,6 +176,9 @@ const char* mkv_status_string(int status) {
         case MKV_ERR_UNSUPPORTED: return "shape not supported by the kernels";
         case MKV_ERR_WORKSPACE: return "workspace missing or too small";
         case MKV_ERR_HIP: return "HIP runtime error (see mkv_last_hip_error)";
+        case MKV_ERR_SCRATCH:
+            return "the call needs more tile-partial space than the no-allocation entry point's fixed "
+                   "device scratch holds (use mkv_mixed_kv_decode_attention with a workspace)";
         default: return "unknown status";
     }
 }
@@ -241,49 +335,26 @@ int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T, int chun
 int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq, const mkv_cache* cache,
                                   const void* tail_k_fp16, const void* tail_v_fp16, int tail_len, int tail_stride,
                                   float* out, void* workspace, size_t workspace_bytes, void* stream) {
-    if (!q_fp16 || !out || !aligned16(q_fp16) || !aligned16(out)) return MKV_ERR_ARG;
-    if (!valid_cache(cache)) return MKV_ERR_ARG;
-    int s = check_cache_shape(cache);
+    int s = attention_args(q_fp16, Hq, cache, tail_k_fp16, tail_v_fp16, tail_len, &tail_stride, out);
     if (s) return s;
-    if (Hq <= 0 || Hq % cache->Hkv != 0) return MKV_ERR_ARG;
-    const int g = Hq / cache->Hkv;
-    if (g != 1 && g != 2 && g != 4) return MKV_ERR_UNSUPPORTED;
-    if ((long)cache->B * Hq > 2147483647L) return MKV_ERR_UNSUPPORTED;
-    if (tail_len < 0 || tail_len >= 4096) return MKV_ERR_ARG;
-    if (tail_len > 0 && (!tail_k_fp16 || !tail_v_fp16)) return MKV_ERR_ARG;
-    if (tail_stride == 0) tail_stride = tail_len;
-    if (tail_stride < tail_len) return MKV_ERR_ARG;
-    {   // the work split counts the cost of the whole cache at capacity in 32-bit granules
-        const int gpi = (512 / cache->d) * mkv::attn_heads_per_row(g) / g;   // group blocks per unit
-        const int bits[3] = {16, 4, 2};
-        long long gran = 0;
-        for (int k = 0; k < 3; ++k) {
-            const long long units = ((long long)cache->cap[k] * (cache->C / mkv::kGroup) + gpi - 1) / gpi;
-            gran += units * ((long long)gpi * mkv::group_bytes(bits[k], cache->d) * mkv::attn_cost16(g, k) /
-                             (16 * mkv::kAttnGranule));
-        }
-        if (gran * cache->B * cache->Hkv > mkv::kAttnMaxGranules) return MKV_ERR_UNSUPPORTED;
-    }
     const size_t need = mkv_workspace_bytes(MKV_OP_ATTENTION, cache->B, Hq, cache->Hkv, cache->d, cache->C, cache->cap);
     if (!workspace || !aligned16(workspace) || workspace_bytes < need) return MKV_ERR_WORKSPACE;
+    return attention_launch(q_fp16, Hq, cache, tail_k_fp16, tail_v_fp16, tail_len, tail_stride, out, workspace,
+                            (hipStream_t)stream);
+}
 
-    mkv::AttnParams ap{};
-    ap.q = static_cast<const uint16_t*>(q_fp16);
-    for (int k = 0; k < 3; ++k) {
-        ap.pool[k] = static_cast<const uint8_t*>(cache->pool[k]);
-        ap.cap[k] = cache->cap[k];
-    }
-    ap.seg_count = cache->seg_count;
-    ap.B = cache->B; ap.Hkv = cache->Hkv; ap.Hq = Hq; ap.C = cache->C;
-    ap.G = attn_workgroups(cache->B, cache->Hkv, cache->d, cache->cap, cache->C);
-    ap.part = static_cast<float*>(workspace);
-    ap.tail_k = static_cast<const uint16_t*>(tail_k_fp16);
-    ap.tail_v = static_cast<const uint16_t*>(tail_v_fp16);
-    ap.tail_len = tail_len;
-    ap.tail_stride = tail_stride;
-    ap.out = out;
-    ap.qscale = (float)(1.4426950408889634 / sqrt((double)cache->d));
-    return hip_status(mkv::launch_attention(ap, cache->d, g, (hipStream_t)stream));
+int mkv_mixed_kv_decode_attention_noalloc(const void* q_fp16, int Hq, const mkv_cache* cache,
+                                          const void* tail_k_fp16, const void* tail_v_fp16, int tail_len,
+                                          int tail_stride, float* out, void* stream) {
+    int s = attention_args(q_fp16, Hq, cache, tail_k_fp16, tail_v_fp16, tail_len, &tail_stride, out);
+    if (s) return s;
+    const size_t need = mkv_workspace_bytes(MKV_OP_ATTENTION, cache->B, Hq, cache->Hkv, cache->d, cache->C, cache->cap);
+    if (need == 0 || need > kScratchBytes) return MKV_ERR_SCRATCH;
+    void* ws = nullptr;
+    s = scratch_of_current_device(&ws);
+    if (s) return s;
+    return attention_launch(q_fp16, Hq, cache, tail_k_fp16, tail_v_fp16, tail_len, tail_stride, out, ws,
+                            (hipStream_t)stream);
 }
 
 int mkv_mixed_kv_prefill_attention(const void* q_fp16, int Hq, int P, const mkv_cache* cache,

@@ -24,6 +24,7 @@ MKV_ERR_ARG = -1
 MKV_ERR_UNSUPPORTED = -2
 MKV_ERR_WORKSPACE = -3
 MKV_ERR_HIP = -4
+MKV_ERR_SCRATCH = -5
 
 MKV_FREEZE_FIRST = 0x1
 MKV_LOGITS_IN = 0x2
@@ -36,7 +37,7 @@ MKV_OP_PREFILL = 4
 
 EXPORTED = (
     "mkv_route_chunks", "mkv_select_chunks_by_similarity", "mkv_quantize_pack_kv",
-    "mkv_mixed_kv_decode_attention", "mkv_mixed_kv_prefill_attention", "mkv_append_tail_rows", "mkv_grow_pool",
+    "mkv_mixed_kv_decode_attention", "mkv_mixed_kv_decode_attention_noalloc", "mkv_mixed_kv_prefill_attention", "mkv_append_tail_rows", "mkv_grow_pool",
     "mkv_workspace_bytes", "mkv_group_bytes", "mkv_pool_bytes",
     "mkv_status_string", "mkv_last_hip_error", "mkv_version",
 )
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.mkv_quantize_pack_kv.restype = i
         L.mkv_mixed_kv_decode_attention.argtypes = [vp, i, ctypes.POINTER(MkvCache), vp, vp, i, i,
                                                     vp, vp, sz, vp]
+        L.mkv_mixed_kv_decode_attention_noalloc.argtypes = [vp, i, ctypes.POINTER(MkvCache), vp, vp, i, i, vp, vp]
+        L.mkv_mixed_kv_decode_attention_noalloc.restype = i
         L.mkv_mixed_kv_prefill_attention.argtypes = [vp, i, i, ctypes.POINTER(MkvCache), vp, vp, vp, vp, sz, vp]
         L.mkv_mixed_kv_prefill_attention.restype = i
         L.mkv_append_tail_rows.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
@@ -444,4 +447,32 @@ def mixed_kv_decode_attention(q: torch.Tensor, cache: PackedCache, out: torch.Te
                                              tail_len, stride, _ptr(out), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "mkv_mixed_kv_decode_attention")
+    return out
+
+
+def mixed_kv_decode_attention_noalloc(q: torch.Tensor, cache: PackedCache, out: torch.Tensor,
+                                      tail_k: torch.Tensor = None, tail_v: torch.Tensor = None,
+                                      tail_len: int = None, stream=None) -> torch.Tensor:
+    """mkv_mixed_kv_decode_attention_noalloc: as mixed_kv_decode_attention,
+    with the tile partials in the library's fixed per-GPU scratch instead of
+    a workspace.  `out` [B, Hq, d] f32 must be given: nothing is allocated."""
+    a = _Args()
+    a.need(q, "q", torch.float16, (cache.B, None, cache.d))
+    B, Hq, d = q.shape
+    a.cache(cache)
+    if (tail_k is None) != (tail_v is None):
+        raise ValueError("tail_k and tail_v go together")
+    a.need(tail_k, "tail_k", torch.float16, (B, cache.Hkv, None, d), optional=True)
+    stride = 0 if tail_k is None else tail_k.shape[2]
+    a.need(tail_v, "tail_v", torch.float16, (B, cache.Hkv, stride, d), optional=True)
+    if tail_len is None:
+        tail_len = stride
+    if not 0 <= tail_len <= stride:
+        raise ValueError(f"tail_len {tail_len} outside the tail's {stride} rows")
+    a.need(out, "out", torch.float32, (B, Hq, d))
+    cc = cache.c()
+    a.on_gpu()
+    st = lib().mkv_mixed_kv_decode_attention_noalloc(_ptr(q), Hq, ctypes.byref(cc), _ptr(tail_k), _ptr(tail_v),
+                                                     tail_len, stride, _ptr(out), _stream(stream))
+    _check(st, "mkv_mixed_kv_decode_attention_noalloc")
     return out

@@ -29,7 +29,9 @@
  *   - Every pointer to tensor data is a DEVICE pointer; structs are passed by
  *     HOST pointer and hold device pointers.  The caller allocates and owns
  *     every buffer and keeps it alive until the stream work is done; the
- *     library allocates nothing and keeps no state between calls.
+ *     library allocates nothing and keeps no state between calls (the one
+ *     exception, the no-allocation variant of call 3, keeps a fixed device
+ *     array per GPU and its address).
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *     the default stream) and the call returns without synchronising.
  *   - Return value: MKV_OK (0) or a negative MKV_ERR_*.  Arguments are
@@ -57,6 +59,8 @@ extern "C" {
 #define MKV_ERR_UNSUPPORTED -2  /* shape outside what the kernels handle    */
 #define MKV_ERR_WORKSPACE   -3  /* workspace missing or too small           */
 #define MKV_ERR_HIP         -4  /* a HIP runtime call failed                */
+#define MKV_ERR_SCRATCH     -5  /* more than the fixed scratch of the
+                                   no-allocation entry point holds           */
 
 /* ---- flags for mkv_route_chunks ---------------------------------------- */
 #define MKV_FREEZE_FIRST 0x1u /* routing freezing: chunk 0 of each sequence
@@ -268,6 +272,35 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq,
                                   const void* tail_v_fp16, int tail_len,
                                   int tail_stride, float* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * 3'. mkv_mixed_kv_decode_attention_noalloc — call 3 without a workspace,
+ *    for callers that cannot allocate device memory (code under HIP graph
+ *    capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, result and limits as mkv_mixed_kv_decode_attention, minus
+ * the workspace: the tile partials go to a fixed device array of
+ * MKV_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held from
+ * the first call on that GPU until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks the array's device address up with that device
+ * current.  The stream must belong to the calling thread's current device.
+ *   Returns MKV_ERR_SCRATCH, before any launch, when the call would need
+ *   more than MKV_NOALLOC_SCRATCH_BYTES of partials, i.e. when
+ *   mkv_workspace_bytes(MKV_OP_ATTENTION, ...) exceeds it (for d = 128
+ *   about (B*Hkv + 256) * (Hq/Hkv) <= 15800).
+ *   Every call on one GPU shares that GPU's array, so calls that overlap in
+ *   time on one GPU (other streams, other threads) race and must not be
+ *   issued; calls on one stream are ordered and safe.  No part of the array
+ *   needs initial contents: each call writes every partial it reads.
+ * ---------------------------------------------------------------------- */
+#define MKV_NOALLOC_SCRATCH_BYTES (8u << 20)
+int mkv_mixed_kv_decode_attention_noalloc(const void* q_fp16, int Hq,
+                                          const mkv_cache* cache,
+                                          const void* tail_k_fp16,
+                                          const void* tail_v_fp16,
+                                          int tail_len, int tail_stride,
+                                          float* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * 3b. mkv_mixed_kv_prefill_attention — chunked prefill over the mixed cache:

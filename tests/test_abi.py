@@ -37,7 +37,7 @@ def test_every_declared_function_is_exported():
 def test_status_strings_and_version():
     L = mkv.lib()
     assert L.mkv_version() >= 1
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert len(L.mkv_status_string(s)) > 0
     assert L.mkv_last_hip_error() == 0
 
@@ -216,3 +216,29 @@ def test_prefill_argument_errors():
     assert prefill() == E.MKV_ERR_WORKSPACE
     assert prefill(ws=0x9000, wsb=64) == E.MKV_ERR_WORKSPACE
     assert mkv.workspace_bytes_prefill(1, 2, 64, 128, 128, [1, 1, 1]) > 0
+
+
+def attn_noalloc(Hq=2, cache=None, tail_len=0, tk=None, tv=None, out=0x700, q=0x600, stride=0):
+    cache = cache or _cache()
+    return mkv.lib().mkv_mixed_kv_decode_attention_noalloc(q, Hq, ctypes.byref(cache), tk, tv, tail_len, stride,
+                                                           out, None)
+
+
+def test_noalloc_attention_argument_errors():
+    """The no-allocation variant checks its arguments like the workspace call
+    and refuses, before any HIP call, a problem whose tile partials exceed
+    its fixed scratch (for callers that cannot allocate device memory)."""
+    E = mkv
+    assert attn_noalloc(q=None) == E.MKV_ERR_ARG
+    assert attn_noalloc(out=0x704) == E.MKV_ERR_ARG
+    assert attn_noalloc(Hq=3) == E.MKV_ERR_ARG
+    assert attn_noalloc(Hq=16) == E.MKV_ERR_UNSUPPORTED
+    assert attn_noalloc(tail_len=5) == E.MKV_ERR_ARG
+    assert attn_noalloc(tail_len=5, tk=0x800, tv=0x900, stride=4) == E.MKV_ERR_ARG
+    big = _cache()
+    big.B, big.Hkv = 1024, 8                         # (8192 + 256) * 4 records of 132 floats > 8 MiB
+    need = mkv.workspace_bytes_attention(1024, 32, 8, 128, 128, [1, 1, 1])
+    assert need > (8 << 20)
+    assert attn_noalloc(Hq=32, cache=big) == E.MKV_ERR_SCRATCH
+    assert mkv.lib().mkv_last_hip_error() == 0       # refused before any HIP call
+    assert b"scratch" in mkv.lib().mkv_status_string(E.MKV_ERR_SCRATCH)
