@@ -2,28 +2,30 @@
 """Throughput of the chunk-adaptive mixed-precision KV path on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input
-of the named workload, one call of each:
-  pack    mkv_quantize_pack_kv   K/V of every chunk -> packed FP16/INT4/INT2 segments
+of the named workload:
   route   mkv_route_chunks       router GEMM (bf16 MFMA) -> vote -> freezing -> reorder
-  attend  mkv_mixed_kv_decode_attention   one decode query per (sequence, head)
+                                 (for the drawn-mix 40-layer shape: vote and reorder of
+                                 per-token scores, no router GEMM)
+  pack    mkv_quantize_pack_kv   K/V of the routed chunks -> packed FP16/INT4/INT2
+                                 segments, once per layer
+  attend  mkv_mixed_kv_decode_attention   one decode query per (sequence, query
+                                 head), once per layer
 
-Inputs are resident in HBM before timing starts.  The routing of the
-synthetic hidden states is the same in every step, so no call depends on
-another call of the same step.  The packed cache is kept in R copies
-(R >= 4, >= 1 GiB in total): step i packs into copy i % R and attends over
-copy (i + 1) % R, whose bytes are identical (same inputs, same deterministic
-kernels) and were written R - 1 steps earlier, so the 256 MB last-level
-cache cannot serve the attention read.  The router runs between the two so
-that the 207 MB just written by the pack (a prefill-time write that a decode
-step does not make) leaves the last-level cache while the router computes,
-not while attention reads.
+The default workload is the largest one that fits one GPU: the llama2-13b
+shape, 40 layers under one shared routing (16 sequences x 8192 tokens, 40
+heads, chunk 128), one decode token per sequence through all 40 layers.
+The llama2-7b layers at 32k and 128k tokens and the llama3-8b GQA append
+step can be named with --workload.
 
-Prints one JSON line.  value = decode-attention effective GB/s (packed KV
-bytes + q + out per launch / attention time); the quantize rate, router rate
-and per-kernel times are reported beside it, and so is the time of the
-alternative selector (mkv_select_chunks_by_similarity: chunk bitwidths from
-the similarity to a query embedding) over the same hidden states, timed on
-its own after the steps.
+Inputs are resident in HBM before timing starts, and no attention read can
+be served by the 256 MB last-level cache (see each workload class).
+
+Prints one JSON line.  value = decode-attention effective GB/s: the packed
+KV + q + out bytes of one layer's attention call divided by that call's
+average time (HIP events around the step's attention calls, launch gaps
+included).  The quantize rate, the router rate and the chunked-prefill and
+similarity-selection times are reported beside it, and so is the oracle on
+the host's cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -49,15 +51,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=configs.LLAMA2_7B_32K.name, choices=[w.name for w in configs.ALL])
+    ap.add_argument("--workload", default=configs.LLAMA2_13B_40L.name,
+                    choices=[w.name for w in configs.ALL if w is not configs.TINY])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle timing on the host (0 disables it)")
     ap.add_argument("--routing-ablation", type=int, default=0, metavar="L",
                     help="also time L-layer steps with routing sharing (one route, L x quantize + attend) "
                          "and without it (every layer routes its own hidden states)")
-    ap.add_argument("--prefill-chunk", type=int, default=256, metavar="P",
-                    help="also time chunked-prefill attention of P new tokens per sequence over the same "
-                         "cache (0 disables)")
+    ap.add_argument("--prefill-chunk", type=int, default=-1, metavar="P",
+                    help="also time chunked-prefill attention of P new tokens per sequence over the (first "
+                         "layer's) cache (default: one chunk; 0 disables)")
     ap.add_argument("--decode-steps", type=int, default=0, metavar="N",
                     help="also time N streaming-decode steps (one token per sequence, full chunks routed, "
                          "quantized and appended) on the grouped-query workload")
@@ -94,53 +97,402 @@ def measured_traffic(workload: str):
     return rec
 
 
-def cpu_baseline(w, k, v, q, tab_bits, budget_s):
-    """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    whole (sequence 0, KV head h) slices, quantized then attended, one thread,
-    head after head (starting over at head 0) until the time budget is spent."""
-    import numpy as np
+# ---------------------------------------------------------------- CPU baseline (the oracle)
+def _cpu_threads() -> int:
+    """Host cores this process may use: its CPU affinity, bounded by the
+    cgroup CPU quota where one is set, and capped at 16 (one GPU's share of
+    a shared box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    for path in ("/sys/fs/cgroup/cpu.max", "/sys/fs/cgroup/cpu/cpu.cfs_quota_us"):
+        try:
+            with open(path) as f:
+                parts = f.read().split()
+            if path.endswith("cpu.max"):
+                if parts[0] != "max":
+                    n = min(n, max(1, int(int(parts[0]) / int(parts[1]))))
+            else:
+                quota = int(parts[0])
+                if quota > 0:
+                    with open("/sys/fs/cgroup/cpu/cpu.cfs_period_us") as f:
+                        n = min(n, max(1, quota // int(f.read().split()[0])))
+            break
+        except (OSError, ValueError, IndexError):
+            continue
+    return max(1, min(16, n))
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _pool_init():
     from threadpoolctl import threadpool_limits
+    globals()["_TPL"] = threadpool_limits(limits=1)     # one BLAS thread per worker process
+
+
+def _oracle_slice(args):
+    """One (sequence, layer, KV head) slice through the oracle: quantize and
+    pack every chunk at its bitwidth, dequantize, and attend with each query
+    head of the GQA group.  Returns (quantize s, attention s, algorithmic
+    attention bytes, tokens)."""
+    import numpy as np
     from chunk_mixed_precision_amd import configs
     from oracle import mkv_oracle as orc
+    kk, vv, qq, bits_row, C, d = args
+    n = len(bits_row)
+    t0 = time.perf_counter()
+    chunks = [orc.quantize_chunk(kk[c * C:(c + 1) * C], vv[c * C:(c + 1) * C], int(bits_row[c])) for c in range(n)]
+    t1 = time.perf_counter()
+    deq = [orc.dequant_chunk(ch) for ch in chunks]
+    kh = np.concatenate([x[0] for x in deq])
+    vh = np.concatenate([x[1] for x in deq])
+    for j in range(qq.shape[0]):
+        orc.attention(qq[j].astype(np.float64), kh, vh)
+    t2 = time.perf_counter()
+    nbytes = sum(configs.chunk_bytes(int(b), d, C) for b in bits_row) + qq.shape[0] * d * 6
+    return t1 - t0, t2 - t1, nbytes, n * C
 
-    bits_row = tab_bits[0]
-    g = w.Hq // w.Hkv
-    t_quant = t_attn = 0.0
-    nbytes = 0
-    heads = 0
-    tokens = 0
-    passes = 0
-    with threadpool_limits(limits=1):
+
+def _oracle_router(args):
+    """Oracle router logits (float64) for a block of tokens; returns seconds."""
+    import numpy as np
+    from oracle import mkv_oracle as orc
+    xb, w12b, w3, b3, inner = args
+    t0 = time.perf_counter()
+    orc.router_logits(orc.bf16_bits_to_f64(xb), orc.bf16_bits_to_f64(w12b), w3, b3, inner)
+    return time.perf_counter() - t0
+
+
+def make_cpu_pool():
+    """Worker processes for the oracle timing, forked before this process
+    touches the GPU (the workers run numpy only)."""
+    import multiprocessing as mp
+    n = _cpu_threads()
+    return mp.get_context("fork").Pool(n, initializer=_pool_init), n
+
+
+def cpu_baseline(pool, ncores, wl, budget_s):
+    """The CPU oracle (as it stands) on a bounded sample of the same
+    workload: whole (sequence, layer, KV head) slices of the bench's own
+    inputs, quantized then attended, each in one worker process with one
+    numpy thread.  One slice first runs alone (the one-thread figures).
+    Waves of 2, 4, ... slices then run side by side to find how many
+    workers the host actually gives this process (the CPU share of a shared
+    box need not show in its affinity mask), and the rest of the budget of
+    about `budget_s` seconds of task time runs at the fastest width.  The
+    slices are copied to the host before any timing; every width is timed
+    by the wall clock around its wave.  For
+    routed workloads the oracle router also runs on blocks of 256 tokens."""
+    gen = wl.cpu_slices()
+    distinct = [next(gen) for _ in range(min(wl.w.Hkv, 8))]     # copied to the host before any timing
+    count = [0]
+
+    def take(k):
+        out = [distinct[(count[0] + j) % len(distinct)] for j in range(k)]
+        count[0] += k
+        return out
+
+    def wave(k):
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_slice, take(k), chunksize=1)
+        return time.perf_counter() - t0, res
+
+    wave(1)                                          # the workers import the oracle once
+    w1, res1 = wave(1)
+    solo = res1[0]
+    spent = solo[0] + solo[1]
+    scan = {1: round(1.0 / w1, 3)}
+    best_k, best_rate = 1, 1.0 / w1
+    k = 2
+    while k <= ncores and spent < budget_s / 2:
+        wall, res = wave(k)
+        spent += sum(r[0] + r[1] for r in res)
+        scan[k] = round(k / wall, 3)
+        if k / wall > best_rate * 1.1:
+            best_k, best_rate = k, k / wall
+        k *= 2
+    tq = ta = 0.0
+    nbytes = tokens = 0
+    wall = 0.0
+    n = 0
+    while n == 0 or (spent < budget_s and wall < budget_s):
+        dt, res = wave(best_k)
+        wall += dt
+        tq += sum(r[0] for r in res)
+        ta += sum(r[1] for r in res)
+        spent += sum(r[0] + r[1] for r in res)
+        nbytes += sum(r[2] for r in res)
+        tokens += sum(r[3] for r in res)
+        n += len(res)
+    out = {
+        "value": round(nbytes / (wall * ta / (tq + ta)) / 1e9, 4), "unit": "GB/s", "cores": best_k, "kind": "oracle",
+        "one_thread_value": round(solo[2] / solo[1] / 1e9, 4),
+        "cpu_model": _cpu_model(),
+        "quantize_tokens_per_s": round(tokens / (wall * tq / (tq + ta)), 1),
+        "quantize_tokens_per_s_one_thread": round(solo[3] / solo[0], 1),
+        "slices_per_s_by_workers": scan,
+    }
+    sample = (f"{n} (sequence, layer, KV head) slices of {wl.w.name} ({wl.slice_desc}), each quantized "
+              f"and packed by the oracle (numpy float32), dequantized and attended in float64 with its "
+              f"{wl.w.group} query head(s); {best_k} worker process(es) side by side (the fastest of "
+              f"1..{ncores} tried), one numpy thread each, {wall:.1f} s wall; value = attention bytes / the "
+              f"attention share of the wall time; one-thread figures from one slice run alone")
+    rt = wl.cpu_router_blocks()
+    if rt is not None:
+        blocks, flop_per_block = rt
+        blocks = blocks[:best_k]
+        solo_r = pool.apply(_oracle_router, (blocks[0],))
+        t0 = time.perf_counter()
+        pool.map(_oracle_router, blocks, chunksize=1)
+        rwall = time.perf_counter() - t0
+        out["router_tflops"] = round(len(blocks) * flop_per_block / rwall / 1e12, 5)
+        out["router_tflops_one_thread"] = round(flop_per_block / solo_r / 1e12, 5)
+        sample += f"; router: {len(blocks)} blocks of 256 tokens in float64 side by side ({rwall:.1f} s wall)"
+    out["sample"] = sample
+    return out
+
+
+# ---------------------------------------------------------------- workloads
+class SingleLayerRouted:
+    """One layer of a routed workload (llama2-7b at 32k or 128k tokens).  A
+    step: route every token (router GEMM, vote, freezing, reorder), quantize
+    and pack the whole prefill with that routing, then one decode attention
+    call.  The packed cache is kept in R copies (R >= 4, >= 1 GiB): step i
+    packs copy i % R and attends over copy (i + 1) % R, whose bytes are
+    identical and were written R - 1 steps earlier, so the 256 MB last-level
+    cache cannot serve the attention read."""
+
+    layers = 1
+
+    def __init__(self, w, dev):
+        import torch
+        from chunk_mixed_precision_amd import mkv, synth
+        self.w = w
+        x, w12, w3, b3 = synth.router_inputs(w)
+        self.x_cpu_bits, self.w12_cpu_bits = x, w12
+        self.x, self.w12, self.w3, self.b3 = x.to(dev), w12.to(dev), w3.to(dev), b3.to(dev)
+        self.k, self.v = synth.kv(w, dev)
+        self.q = synth.query(w, dev)
+        self.tab = mkv.RouteTables(w.B, w.n, dev)
+        self.ws_route = torch.empty(mkv.workspace_bytes_route(w.B, w.T, w.D, w.I), dtype=torch.uint8, device=dev)
+        mkv.route_chunks(self.tab, w.C, x=self.x, w12=self.w12, w3=self.w3, b3=self.b3, workspace=self.ws_route)
+        torch.cuda.synchronize()
+        self.seg = self.tab.seg_count.cpu().numpy()
+        self.caps = [int(self.seg[:, kk].max()) for kk in range(3)]
+        one = mkv.PackedCache(w.B, w.Hkv, w.d, w.C, self.caps, self.tab.seg_count, dev)
+        self.R = max(4, math.ceil((1 << 30) / one.nbytes()))
+        self.caches = [one] + [mkv.PackedCache(w.B, w.Hkv, w.d, w.C, self.caps, self.tab.seg_count, dev)
+                               for _ in range(self.R - 1)]
+        for c in self.caches:
+            mkv.quantize_pack_kv(self.k, self.v, self.tab, c)
+        self.ws_attn = mkv.attention_workspace(w.B, w.Hq, one, dev)
+        self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+        self.route_tokens = w.B * w.T
+        self.pack_tokens = w.B * w.T
+        self.slice_desc = f"sequence 0, {w.T} tokens per head"
+
+    def step(self, i, e):
+        from chunk_mixed_precision_amd import mkv
+        w = self.w
+        e and e[0].record()
+        mkv.route_chunks(self.tab, w.C, x=self.x, w12=self.w12, w3=self.w3, b3=self.b3, workspace=self.ws_route)
+        e and e[1].record()
+        mkv.quantize_pack_kv(self.k, self.v, self.tab, self.caches[i % self.R])
+        e and e[2].record()
+        mkv.mixed_kv_decode_attention(self.q, self.caches[(i + 1) % self.R], out=self.out, workspace=self.ws_attn)
+        e and e[3].record()
+
+    def attention_cache(self):
+        return self.caches[0]
+
+    def cpu_slices(self):
+        w = self.w
+        bits = self.tab.chunk_bits.cpu().numpy()[0, :w.n]
+        g = w.group
         for i in range(1 << 30):
             h = i % w.Hkv
-            passes += h == 0
-            kk = k[0, h].cpu().numpy()
-            vv = v[0, h].cpu().numpy()
-            qq = q[0, h * g:(h + 1) * g].cpu().numpy()
-            t0 = time.perf_counter()
-            chunks = [orc.quantize_chunk(kk[c * w.C:(c + 1) * w.C], vv[c * w.C:(c + 1) * w.C], int(bits_row[c]))
-                      for c in range(w.n)]
-            t1 = time.perf_counter()
-            deq = [orc.dequant_chunk(ch) for ch in chunks]
-            kh = np.concatenate([d[0] for d in deq])
-            vh = np.concatenate([d[1] for d in deq])
-            for j in range(g):
-                orc.attention(qq[j].astype(np.float64), kh, vh)
-            t2 = time.perf_counter()
-            t_quant += t1 - t0
-            t_attn += t2 - t1
-            nbytes += sum(configs.chunk_bytes(int(b), w.d, w.C) for b in bits_row[:w.n]) + g * w.d * 6
-            tokens += w.T
-            heads += 1
-            if t_quant + t_attn >= budget_s:
-                break
-    return {
-        "value": round(nbytes / t_attn / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"sequence 0 of {w.name}, {heads} (sequence, KV head) slices in {passes} pass(es) over its "
-                   f"{w.Hkv} KV heads: oracle dequant + fp64 attention over {w.T} tokens per head "
-                   f"({t_attn:.1f} s); oracle quantize of the same slices {tokens / t_quant:.0f} tokens/s per "
-                   f"head-slice ({t_quant:.1f} s); numpy, 1 thread"),
-    }
+            yield (self.k[0, h].cpu().numpy(), self.v[0, h].cpu().numpy(),
+                   self.q[0, h * g:(h + 1) * g].cpu().numpy(), bits, w.C, w.d)
+
+    def cpu_router_blocks(self):
+        import numpy as np
+        import torch
+        w = self.w
+        xb = self.x_cpu_bits.reshape(-1, w.D).view(torch.int16).numpy().view(np.uint16)
+        wb = self.w12_cpu_bits.view(torch.int16).numpy().view(np.uint16)
+        w3 = self.w3.cpu().numpy().astype(np.float64)
+        b3 = self.b3.cpu().numpy().astype(np.float64)
+        blocks = [(xb[j * 256:(j + 1) * 256], wb, w3, b3, w.I) for j in range(_cpu_threads())]
+        return blocks, 256 * (2.0 * w.D * 2 * w.I + 2.0 * w.I * 3)
+
+
+class MultiLayerShared:
+    """The llama2-13b shape: 40 layers under one routing (routing sharing),
+    each with its own K, V and query.  The chunk bitwidths are drawn per
+    sequence (no router is run for this shape); a step votes and reorders
+    them (logits-in route: each token's scores pick its chunk's drawn
+    expert, then the chunk vote, freezing and the stable reorder), quantizes
+    and packs every layer's prefill into that layer's cache, then runs one
+    decode attention call per layer.  Attention of layer l reads the cache
+    written 40 quantize calls and l attention calls earlier (40 GB of other
+    traffic), which the 256 MB last-level cache cannot serve."""
+
+    def __init__(self, w, dev):
+        import torch
+        from chunk_mixed_precision_amd import mkv, synth
+        self.w = w
+        self.layers = w.layers
+        experts = synth.drawn_chunk_experts(w)
+        self.logits = synth.one_hot_logits(experts, w.C).to(dev)
+        self.tab = mkv.RouteTables(w.B, w.n, dev)
+        mkv.route_chunks(self.tab, w.C, logits=self.logits, logits_in=True)
+        torch.cuda.synchronize()
+        self.seg = self.tab.seg_count.cpu().numpy()
+        self.caps = [int(self.seg[:, kk].max()) for kk in range(3)]
+        self.kv = []
+        self.q = []
+        self.caches = []
+        for l in range(w.layers):
+            self.kv.append(synth.kv(w, dev, layer=l))
+            self.q.append(synth.query(w, dev, layer=l))
+            self.caches.append(mkv.PackedCache(w.B, w.Hkv, w.d, w.C, self.caps, self.tab.seg_count, dev))
+            mkv.quantize_pack_kv(self.kv[l][0], self.kv[l][1], self.tab, self.caches[l])
+        self.R = 1
+        self.ws_attn = mkv.attention_workspace(w.B, w.Hq, self.caches[0], dev)
+        self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+        self.route_tokens = w.B * w.T
+        self.pack_tokens = w.B * w.T
+        self.slice_desc = f"sequence 0 of layer 0, {w.T} tokens per head"
+
+    def step(self, i, e):
+        from chunk_mixed_precision_amd import mkv
+        w = self.w
+        e and e[0].record()
+        mkv.route_chunks(self.tab, w.C, logits=self.logits, logits_in=True)
+        e and e[1].record()
+        for l in range(self.layers):
+            mkv.quantize_pack_kv(self.kv[l][0], self.kv[l][1], self.tab, self.caches[l])
+        e and e[2].record()
+        for l in range(self.layers):
+            mkv.mixed_kv_decode_attention(self.q[l], self.caches[l], out=self.out, workspace=self.ws_attn)
+        e and e[3].record()
+
+    def attention_cache(self):
+        return self.caches[0]
+
+    def cpu_slices(self):
+        w = self.w
+        bits = self.tab.chunk_bits.cpu().numpy()[0, :w.n]
+        k, v = self.kv[0]
+        for i in range(1 << 30):
+            h = i % w.Hkv
+            yield (k[0, h].cpu().numpy(), v[0, h].cpu().numpy(), self.q[0][0, h:h + 1].cpu().numpy(), bits,
+                   w.C, w.d)
+
+    def cpu_router_blocks(self):
+        return None
+
+
+class AppendStep:
+    """The llama3-8b GQA shape: 64 sequences with 8192 tokens prefilled
+    (drawn chunk mix, chunk 0 FP16), and per step one new 256-token chunk
+    per sequence: route its 16384 tokens (router GEMM, vote and reorder of
+    all 33 chunks, append mode), quantize and pack it into its segment
+    (slot of chunk 32, rewritten every step, so the state stays the same),
+    then decode attention over 8448 tokens (32 query heads over 8 KV heads).
+    The cache is kept in R copies (>= 1 GiB), rotated as for one layer."""
+
+    layers = 1
+
+    def __init__(self, w, dev):
+        import torch
+        from chunk_mixed_precision_amd import mkv, synth
+        self.w = w
+        experts = synth.drawn_chunk_experts(w)
+        experts[:, 0] = 0
+        self.tab = mkv.RouteTables(w.B, w.n_total, dev)
+        mkv.route_chunks(self.tab, w.C, logits=synth.one_hot_logits(experts, w.C).to(dev), logits_in=True)
+        x, w12, w3, b3 = synth.router_inputs(w, tokens_per_seq=w.C, chunk_offset=w.n)
+        self.x_cpu_bits, self.w12_cpu_bits = x, w12
+        self.x, self.w12, self.w3, self.b3 = x.to(dev), w12.to(dev), w3.to(dev), b3.to(dev)
+        self.ws_route = torch.empty(mkv.workspace_bytes_route(w.B, w.C, w.D, w.I), dtype=torch.uint8, device=dev)
+        mkv.route_chunks(self.tab, w.C, x=self.x, w12=self.w12, w3=self.w3, b3=self.b3, workspace=self.ws_route,
+                         append=True, chunk_offset=w.n)
+        torch.cuda.synchronize()
+        self.seg = self.tab.seg_count.cpu().numpy()
+        self.caps = [int(self.seg[:, kk].max()) for kk in range(3)]
+        k, v = synth.kv(w, dev)
+        self.ka, self.va = synth.kv(w, dev, tokens=w.C, token_offset_stream=1)
+        self.q = synth.query(w, dev)
+        one = mkv.PackedCache(w.B, w.Hkv, w.d, w.C, self.caps, self.tab.seg_count, dev)
+        self.R = max(4, math.ceil((1 << 30) / one.nbytes()))
+        self.caches = [one] + [mkv.PackedCache(w.B, w.Hkv, w.d, w.C, self.caps, self.tab.seg_count, dev)
+                               for _ in range(self.R - 1)]
+        for c in self.caches:
+            mkv.quantize_pack_kv(k, v, self.tab, c)
+            mkv.quantize_pack_kv(self.ka, self.va, self.tab, c, chunk_offset=w.n)
+        self.k_cpu_src = (k, v)
+        self.ws_attn = mkv.attention_workspace(w.B, w.Hq, one, dev)
+        self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+        self.route_tokens = w.B * w.C
+        self.pack_tokens = w.B * w.C
+        self.slice_desc = f"sequence 0, {w.T} prefilled tokens per KV head"
+
+    def step(self, i, e):
+        from chunk_mixed_precision_amd import mkv
+        w = self.w
+        e and e[0].record()
+        mkv.route_chunks(self.tab, w.C, x=self.x, w12=self.w12, w3=self.w3, b3=self.b3, workspace=self.ws_route,
+                         append=True, chunk_offset=w.n)
+        e and e[1].record()
+        mkv.quantize_pack_kv(self.ka, self.va, self.tab, self.caches[i % self.R], chunk_offset=w.n)
+        e and e[2].record()
+        mkv.mixed_kv_decode_attention(self.q, self.caches[(i + 1) % self.R], out=self.out, workspace=self.ws_attn)
+        e and e[3].record()
+
+    def attention_cache(self):
+        return self.caches[0]
+
+    def cpu_slices(self):
+        w = self.w
+        bits = self.tab.chunk_bits.cpu().numpy()[0, :w.n]
+        k, v = self.k_cpu_src
+        g = w.group
+        for i in range(1 << 30):
+            h = i % w.Hkv
+            yield (k[0, h].cpu().numpy(), v[0, h].cpu().numpy(), self.q[0, h * g:(h + 1) * g].cpu().numpy(), bits,
+                   w.C, w.d)
+
+    def cpu_router_blocks(self):
+        import numpy as np
+        import torch
+        w = self.w
+        xb = self.x_cpu_bits.reshape(-1, w.D).view(torch.int16).numpy().view(np.uint16)
+        wb = self.w12_cpu_bits.view(torch.int16).numpy().view(np.uint16)
+        w3 = self.w3.cpu().numpy().astype(np.float64)
+        b3 = self.b3.cpu().numpy().astype(np.float64)
+        blocks = [(xb[j * 256:(j + 1) * 256], wb, w3, b3, w.I) for j in range(_cpu_threads())]
+        return blocks, 256 * (2.0 * w.D * 2 * w.I + 2.0 * w.I * 3)
+
+
+def make_workload(w, dev):
+    if w.layers > 1:
+        return MultiLayerShared(w, dev)
+    if w.append_chunks:
+        return AppendStep(w, dev)
+    if w.routed:
+        return SingleLayerRouted(w, dev)
+    raise SystemExit(f"bench.py does not time {w.name}: it fits the last-level cache (a parity-test case)")
 
 
 def routing_ablation(w, L, steps, warmup):
@@ -256,39 +608,22 @@ def main():
               "(pass --gpus 1; sharding is described in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
 
+    # the oracle's worker processes are forked before anything touches the GPU
+    pool, ncores = make_cpu_pool() if args.cpu_seconds > 0 else (None, 0)
+
     import numpy as np
     import torch
 
     from chunk_mixed_precision_amd import configs, mkv, synth
 
     w = configs.BY_NAME[args.workload]
-    if not w.routed or w.append_chunks or w.layers != 1:
-        print(f"bench.py times the single-layer routed workloads; {w.name} is a parity-test case",
-              file=sys.stderr)
-        sys.exit(2)
     dev = "cuda"
     torch.cuda.set_device(0)
     mkv.lib()
 
-    # ---------------- inputs, resident in HBM
-    x, w12, w3, b3 = synth.router_inputs(w)
-    x, w12, w3, b3 = x.to(dev), w12.to(dev), w3.to(dev), b3.to(dev)
-    k, v = synth.kv(w, dev)
-    q = synth.query(w, dev)
-    tab = mkv.RouteTables(w.B, w.n, dev)
-    ws_route = torch.empty(mkv.workspace_bytes_route(w.B, w.T, w.D, w.I), dtype=torch.uint8, device=dev)
-    mkv.route_chunks(tab, w.C, x=x, w12=w12, w3=w3, b3=b3, workspace=ws_route)
-    torch.cuda.synchronize()
-    seg = tab.seg_count.cpu().numpy()
-    caps = [int(seg[:, kk].max()) for kk in range(3)]
-    one = mkv.PackedCache(w.B, w.Hkv, w.d, w.C, caps, tab.seg_count, dev)
-    cache_bytes = one.nbytes()
-    R = max(4, math.ceil((1 << 30) / cache_bytes))
-    caches = [one] + [mkv.PackedCache(w.B, w.Hkv, w.d, w.C, caps, tab.seg_count, dev) for _ in range(R - 1)]
-    for c in caches:
-        mkv.quantize_pack_kv(k, v, tab, c)
-    ws_attn = mkv.attention_workspace(w.B, w.Hq, one, dev)
-    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    # ---------------- inputs, resident in HBM; tables and caches built once
+    wl = make_workload(w, dev)
+    seg, caps = wl.seg, wl.caps
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -298,53 +633,47 @@ def main():
 
     nev = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nev)]
-
-    # one step in the order of the data flow: route and vote, quantize/pack with that routing,
-    # then decode attention.  Attention reads the cache copy written R - 1 steps earlier, so the
-    # bytes quantize has just written cannot serve it from the last-level cache.
-    def step(i, rec):
-        e = ev[i] if rec else None
-        if e:
-            e[0].record()
-        mkv.route_chunks(tab, w.C, x=x, w12=w12, w3=w3, b3=b3, workspace=ws_route)
-        if e:
-            e[1].record()
-        mkv.quantize_pack_kv(k, v, tab, caches[i % R])
-        if e:
-            e[2].record()
-        mkv.mixed_kv_decode_attention(q, caches[(i + 1) % R], out=out, workspace=ws_attn)
-        if e:
-            e[3].record()
-
     for i in range(args.warmup):
-        step(i, False)
+        wl.step(i, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, True)
+        wl.step(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # the alternative selector (similarity to a query embedding) on the same hidden states
-    qe = synth.query_embedding(w).to(dev)
-    tab_sim = mkv.RouteTables(w.B, w.n, dev)
-    ws_sim = torch.empty(mkv.workspace_bytes_similarity(w.B, w.T, w.D, w.C), dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        mkv.select_chunks_by_similarity(tab_sim, w.C, x, qe, 0.3, 0.0, workspace=ws_sim)
-    ev_sim = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
-    for i in range(nev):
-        ev_sim[i][0].record()
-        mkv.select_chunks_by_similarity(tab_sim, w.C, x, qe, 0.3, 0.0, workspace=ws_sim)
-        ev_sim[i][1].record()
-    torch.cuda.synchronize()
-    t_sim = np.array([a.elapsed_time(b) for a, b in ev_sim]) * 1e-3
-    sim_bytes = w.B * w.T * w.D * 2 + w.B * w.D * 2 + w.B * w.n * (1 + 4 + 4)
+    t_route = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
+    t_pack = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
+    t_attn = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(nev)]) * 1e-3
 
-    # chunked prefill: P new tokens per sequence attend over the same caches (rotated) and causally
-    # over themselves, on the matrix cores
+    # the alternative selector (similarity to a query embedding) on the same hidden states
+    sim = None
+    if isinstance(wl, SingleLayerRouted):
+        qe = synth.query_embedding(w).to(dev)
+        tab_sim = mkv.RouteTables(w.B, w.n, dev)
+        ws_sim = torch.empty(mkv.workspace_bytes_similarity(w.B, w.T, w.D, w.C), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            mkv.select_chunks_by_similarity(tab_sim, w.C, wl.x, qe, 0.3, 0.0, workspace=ws_sim)
+        ev_sim = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
+        for i in range(nev):
+            ev_sim[i][0].record()
+            mkv.select_chunks_by_similarity(tab_sim, w.C, wl.x, qe, 0.3, 0.0, workspace=ws_sim)
+            ev_sim[i][1].record()
+        torch.cuda.synchronize()
+        t_sim = float(np.mean([a.elapsed_time(b) for a, b in ev_sim])) * 1e-3
+        sim_bytes = w.B * w.T * w.D * 2 + w.B * w.D * 2 + w.B * w.n * (1 + 4 + 4)
+        sim = {"us": round(t_sim * 1e6, 2),
+               "roofline": {"bound": "hbm", "achieved": round(sim_bytes / t_sim / 1e9, 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(sim_bytes / t_sim / 1e9 / HBM_PEAK_GBS, 4),
+                            "bytes_per_launch": sim_bytes}}
+        del tab_sim, ws_sim
+
+    # chunked prefill: P new tokens per sequence attend over the (first layer's) cache and causally over
+    # themselves, on the matrix cores
     pre = None
-    if args.prefill_chunk > 0:
-        Pn = args.prefill_chunk
+    Pn = w.C if args.prefill_chunk < 0 else args.prefill_chunk
+    if Pn > 0:
+        cache0 = wl.attention_cache()
         gq = torch.Generator(device=dev)
         gq.manual_seed(w.seed * 100 + 55)
         pq = torch.randn((w.B, w.Hq, Pn, w.d), generator=gq, device=dev).to(torch.float16)
@@ -353,19 +682,20 @@ def main():
         pout = torch.empty((w.B, w.Hq, Pn, w.d), dtype=torch.float32, device=dev)
         pws = torch.empty(mkv.workspace_bytes_prefill(w.B, w.Hq, Pn, w.d, w.C, caps), dtype=torch.uint8, device=dev)
         for i in range(3):
-            mkv.mixed_kv_prefill_attention(pq, caches[i % R], pkn, pvn, out=pout, workspace=pws)
-        ev_pre = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
-        for i in range(nev):
+            mkv.mixed_kv_prefill_attention(pq, cache0, pkn, pvn, out=pout, workspace=pws)
+        npre = max(3, min(nev, 10))
+        ev_pre = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(npre)]
+        for i in range(npre):
             ev_pre[i][0].record()
-            mkv.mixed_kv_prefill_attention(pq, caches[i % R], pkn, pvn, out=pout, workspace=pws)
+            mkv.mixed_kv_prefill_attention(pq, cache0, pkn, pvn, out=pout, workspace=pws)
             ev_pre[i][1].record()
         torch.cuda.synchronize()
         t_pre = float(np.mean([a.elapsed_time(b) for a, b in ev_pre])) * 1e-3
-        ctx = w.T
-        pre_flop = 4.0 * w.B * w.Hq * Pn * w.d * (ctx + (Pn + 1) / 2.0)
+        ctx = int(seg.sum(1).max()) * w.C
+        pre_flop = 4.0 * w.Hq * Pn * w.d * (float(seg.sum(1).sum()) * w.C + w.B * (Pn + 1) / 2.0)
         pre_bytes = (configs.effective_attention_bytes(w, seg) - w.B * w.Hq * w.d * 6
                      + w.B * w.Hq * Pn * w.d * (2 + 4) + 2 * w.B * w.Hkv * Pn * w.d * 2)
-        pre = {"P": Pn, "us": round(t_pre * 1e6, 2),
+        pre = {"P": Pn, "context": ctx, "us": round(t_pre * 1e6, 2),
                "roofline": {"bound": "mfma", "achieved": round(pre_flop / t_pre / 1e12, 2),
                             "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(pre_flop / t_pre / 1e12 / FP16_PEAK_TFLOPS, 4),
@@ -388,19 +718,41 @@ def main():
     copy_gbs = 2 * cp_bytes / (float(np.median([a.elapsed_time(b) for a, b in ev_cp])) * 1e-3) / 1e9
     del csrc, cdst
 
-    t_route = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nev)]) * 1e-3
-    t_pack = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nev)]) * 1e-3
-    t_attn = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(nev)]) * 1e-3
-
-    attn_bytes = configs.effective_attention_bytes(w, seg)
+    L = wl.layers
+    attn_bytes = configs.effective_attention_bytes(w, seg)          # one layer's call
     traffic = measured_traffic(w.name)
-    pack_read = w.B * w.Hkv * w.T * w.d * 2 * 2
-    pack_write = sum(int(seg[b, kk]) * configs.chunk_bytes(bits, w.d, w.C) * w.Hkv
-                     for b in range(w.B) for kk, bits in enumerate(configs.EXPERT_BITS))
-    router_flop = 2.0 * w.B * w.T * w.D * 2 * w.I + 2.0 * w.B * w.T * w.I * 3
-    a_mean = float(t_attn.mean())
-    attn_gbs = attn_bytes / a_mean / 1e9
+    pack_tokens = wl.pack_tokens                                    # per layer and step
+    pack_read = pack_tokens * w.Hkv * w.d * 2 * 2
+    if isinstance(wl, AppendStep):
+        new = wl.tab.chunk_bits.cpu().numpy()[:, w.n]
+        pack_write = sum(configs.chunk_bytes(int(b), w.d, w.C) * w.Hkv for b in new)
+    else:
+        pack_write = sum(int(seg[b, kk]) * configs.chunk_bytes(bits, w.d, w.C) * w.Hkv
+                         for b in range(w.B) for kk, bits in enumerate(configs.EXPERT_BITS))
+    a_call = float(t_attn.mean()) / L                               # average duration of one layer's call
+    attn_gbs = attn_bytes / a_call / 1e9
+    p_call = float(t_pack.mean()) / L
     avg_bits = float(sum(seg[:, kk].sum() * bits for kk, bits in enumerate(configs.EXPERT_BITS)) / seg.sum())
+    route = {"us": round(float(t_route.mean()) * 1e6, 2), "tokens": wl.route_tokens}
+    if w.routed:
+        router_flop = 2.0 * wl.route_tokens * w.D * 2 * w.I + 2.0 * wl.route_tokens * w.I * 3
+        route["roofline"] = {"bound": "mfma", "achieved": round(router_flop / float(t_route.mean()) / 1e12, 2),
+                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(router_flop / float(t_route.mean()) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                             "flop_per_launch": router_flop}
+    else:
+        route["note"] = ("drawn chunk mix: the route call votes and reorders per-token scores (logits-in), "
+                         "no router GEMM")
+
+    cfg = {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+           "context": int(seg.sum(1).max()) * w.C, "chunk": w.C, "layers": L,
+           "chunk_mix": [int(x) for x in seg.sum(0)], "avg_bits": round(avg_bits, 3)}
+    if w.routed:
+        cfg.update(router_hidden=w.D, router_inner=w.I)
+    if w.append_chunks:
+        cfg["appended_chunks_per_step"] = w.append_chunks
+    if wl.R > 1:
+        cfg["cache_copies"] = wl.R
 
     res = {
         "metric": "mixed-KV decode attention effective HBM GB/s (% of peak) + quantize tokens/s",
@@ -415,38 +767,30 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic (seeded), random-init router",
-        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
-                   "context": w.T, "chunk": w.C, "router_hidden": w.D, "router_inner": w.I,
-                   "chunk_mix": [int(s) for s in seg.sum(0)], "avg_bits": round(avg_bits, 3),
-                   "cache_copies": R},
+        "config": cfg,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_call"],
                      "kernel": "mkv_mixed_kv_decode_attention call (attn_tile_kernel + attn_combine_kernel)",
-                     "bytes_per_launch": attn_bytes, "avg_launch_us": round(a_mean * 1e6, 3)},
-        "quantize_tokens_per_s": round(w.B * w.T / float(t_pack.mean()), 1),
+                     "bytes_per_launch": attn_bytes, "launches_per_step": L,
+                     "avg_launch_us": round(a_call * 1e6, 3)},
+        "quantize_tokens_per_s": round(pack_tokens / p_call, 1),
         "device_copy": {"gbs": round(copy_gbs, 1), "bytes_moved": 2 * cp_bytes,
                         "attention_frac_of_copy": round(attn_gbs / copy_gbs, 4)},
         "kernels": {
-            "route": {"us": round(float(t_route.mean()) * 1e6, 2),
-                      "roofline": {"bound": "mfma", "achieved": round(router_flop / float(t_route.mean()) / 1e12, 2),
-                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                   "frac": round(router_flop / float(t_route.mean()) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                                   "flop_per_launch": router_flop}},
-            "pack": {"us": round(float(t_pack.mean()) * 1e6, 2),
-                     "roofline": {"bound": "hbm", "achieved": round((pack_read + pack_write) / float(t_pack.mean()) / 1e9, 2),
+            "route": route,
+            "pack": {"us_per_layer": round(p_call * 1e6, 2), "layers": L,
+                     "roofline": {"bound": "hbm", "achieved": round((pack_read + pack_write) / p_call / 1e9, 2),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round((pack_read + pack_write) / float(t_pack.mean()) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "frac": round((pack_read + pack_write) / p_call / 1e9 / HBM_PEAK_GBS, 4),
                                   "bytes_per_launch": pack_read + pack_write}},
-            "select_similarity": {
-                "us": round(float(t_sim.mean()) * 1e6, 2),
-                "roofline": {"bound": "hbm", "achieved": round(sim_bytes / float(t_sim.mean()) / 1e9, 2),
-                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(sim_bytes / float(t_sim.mean()) / 1e9 / HBM_PEAK_GBS, 4),
-                             "bytes_per_launch": sim_bytes}},
+            "select_similarity": sim,
             "prefill_attend": pre,
-            "attend": {"us": round(a_mean * 1e6, 2), "us_p10": round(float(np.percentile(t_attn, 10)) * 1e6, 2),
-                       "us_p90": round(float(np.percentile(t_attn, 90)) * 1e6, 2), "bytes": attn_bytes,
+            "attend": {"us_per_layer": round(a_call * 1e6, 2),
+                       "us_per_step": round(float(t_attn.mean()) * 1e6, 2),
+                       "us_per_step_p10": round(float(np.percentile(t_attn, 10)) * 1e6, 2),
+                       "us_per_step_p90": round(float(np.percentile(t_attn, 90)) * 1e6, 2),
+                       "bytes_per_layer": attn_bytes, "bytes_per_step": attn_bytes * L,
                        "traffic": None if traffic is None else {
                            "bytes_per_call": traffic["bytes_per_call"],
                            "ratio_to_algorithmic": traffic["ratio_to_algorithmic"],
@@ -456,13 +800,19 @@ def main():
         },
     }
     if args.routing_ablation > 0:
-        del caches, x
+        del wl
         torch.cuda.empty_cache()
-        res["routing_ablation"] = routing_ablation(w, args.routing_ablation, max(3, args.steps // 4), 2)
+        wa = w if (w.routed and w.layers == 1 and not w.append_chunks) else configs.LLAMA2_7B_32K
+        res["routing_ablation"] = routing_ablation(wa, args.routing_ablation, max(3, args.steps // 4), 2)
+        wl = None
     if args.decode_steps > 0:
         res["streaming_decode"] = streaming_decode(args.decode_steps)
-    if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(w, k, v, q, tab.chunk_bits.cpu().numpy(), args.cpu_seconds)
+    if pool is not None:
+        if wl is None:
+            wl = make_workload(w, dev)
+        res["cpu_baseline"] = cpu_baseline(pool, ncores, wl, args.cpu_seconds)
+        pool.close()
+        pool.join()
     print(json.dumps(res), flush=True)
 
 
