@@ -29,7 +29,8 @@ constexpr int NWAVE = 8;                // wavefronts per workgroup (2 per SIMD)
 constexpr int PT = 64 * NWAVE;          // threads per workgroup
 constexpr int QPW = 32;                 // queries per wavefront
 constexpr int QT = QPW * NWAVE;         // queries per workgroup
-constexpr int RING_CELLS = 6144;        // 96 KB ring of raw group blocks (16-byte cells)
+constexpr int RING_CELLS = 4096;        // 64 KB ring of raw group-block pairs (16-byte cells)
+constexpr int DQ_THREADS = PT / 2;      // threads that dequantize one group block of a pair
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glob_void;
@@ -89,8 +90,8 @@ __device__ __forceinline__ const _Float16* vt_at(const PfTile<D>& s, int ch, int
 
 template <int D>
 struct PfLds {
-    u32x4 ring[RING_CELLS];                // raw group blocks in flight (slots sized per bitwidth)
-    PfTile<D> tile[2];                     // fp16 blocks: one being consumed, one being filled
+    u32x4 ring[RING_CELLS];                // raw group-block pairs in flight (slots sized per bitwidth)
+    PfTile<D> tile[2][2];                  // fp16 block pairs: one being consumed, one being filled
 };
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -132,19 +133,18 @@ __device__ __forceinline__ uint32_t mix_pair(uint32_t ya, uint32_t yb, float wa,
 // for the values (gathered from the four lane slots that hold tokens
 // 4m .. 4m+3 of a value group).
 template <int D, int BITS>
-__device__ __forceinline__ void dequant_block(PfTile<D>& s, const u32x4* raw) {
+__device__ __forceinline__ void dequant_block(PfTile<D>& s, const u32x4* raw, int tid) {
     constexpr int S = D / 8, NG = D / 32;
-    const int tid = threadIdx.x;
     if constexpr (BITS == 16) {
         // keys: row r, lane slot L: channels 8L..8L+7 of token tok(L, r)
-        for (int c = tid; c < 32 * S; c += PT) {
+        for (int c = tid; c < 32 * S; c += DQ_THREADS) {
             const int r = c / S, L = c % S;
             *reinterpret_cast<u32x4*>(&s.k[tok_of(S, L, r)][8 * L]) = raw[c];
         }
         // values: item (m, G, octet o, half h): channels 32G + 8o + 4h .. +3 of
         // tokens 4m .. 4m+3, i.e. of token m of the slots tq*NG + G, tq = 0..3
         // (row 4m + o holds channels 32G + 8o .. +7 of the slot's token m)
-        for (int c = tid; c < 8 * NG * 4 * 2; c += PT) {
+        for (int c = tid; c < 8 * NG * 4 * 2; c += DQ_THREADS) {
             const int m = c & 7, G = (c >> 3) % NG, o = (c / (8 * NG)) & 3, h = c / (32 * NG);
             uint32_t w[4][2];
 #pragma unroll
@@ -212,7 +212,8 @@ __device__ __forceinline__ void dequant_block(PfTile<D>& s, const u32x4* raw) {
         constexpr int VH = BITS == 4 ? 1 : 2;   // value items per word (channels split in halves)
         constexpr int NV = 8 * NG * NW * VH;
         constexpr int FPI = F / KH;             // fields per item (8)
-        static_assert(NK % 64 == 0 && NV % 64 == 0 && NK + NV <= PT, "one item per thread, wave-uniform kinds");
+        static_assert(NK % 64 == 0 && NV % 64 == 0 && NK + NV <= DQ_THREADS,
+                      "one item per thread, wave-uniform kinds");
         static_assert(F / KH == 8 && F / VH == 8, "eight fields per item");
         if (tid < NK) {
             // keys: cell (code row, slot L) = channels 8L + 4(row&1) .. +3; its
@@ -386,48 +387,61 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, floa
             w.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[t][ks2], ks2 ? pf1 : pf0, w.o[t], 0, 0, 0);
 }
 
-// Group blocks [lo, hi) of one bitwidth segment.  Raw blocks stream into a
-// ring of NR slots by direct global->LDS loads issued NR blocks ahead (one
-// block per iteration, re-reading the last block once the segment is
-// exhausted, so the number of loads in flight and hence every wait count is
-// fixed).  Iteration g dequantizes block g+1 into one fp16 tile while the
-// matrix cores consume block g from the other, with one barrier between
-// iterations.
+// Group blocks [lo, hi) of one bitwidth segment, two at a time.  Raw
+// block pairs (adjacent in the pool) stream into a ring of NR slots by
+// direct global->LDS loads issued NR pairs ahead (one pair per iteration,
+// re-reading the last pair once the segment is exhausted, so the number of
+// loads in flight and hence every wait count is fixed).  Iteration j
+// dequantizes pair j+1 into one pair of fp16 tiles -- threads 0 .. PT/2-1
+// the first block, the others the second -- while the matrix cores consume
+// pair j from the other, with one barrier between iterations: the barrier,
+// the ring traffic and the dequant latency are paid once per 64 tokens.
+// A pair whose second block lies past hi (an odd count) has only its first
+// block dequantized and attended.
 template <int D, int BITS>
 __device__ __forceinline__ void pf_segment(PfState<D>& w, PfLds<D>& s, const uint8_t* seg_base, int lo, int hi,
                                            float qscale, int qp, int P) {
     constexpr int S = D / 8;
     constexpr int NC = group_rows(BITS) * S;       // 16-byte cells per block
-    constexpr int LPW = (NC + PT - 1) / PT;        // 64-cell loads per wavefront and block
+    constexpr int LPW = (2 * NC + PT - 1) / PT;    // 64-cell loads per wavefront and pair
     constexpr int SLOT = LPW * PT;                 // cells per ring slot
     constexpr int NR = RING_CELLS / SLOT;          // ring slots
     constexpr int GC = (int)(group_bytes(BITS, D) / 16);
-    static_assert(NR >= 3 && (NR - 1) * LPW < 64, "ring depth");
+    static_assert(GC == NC && NR >= 2 && (NR - 1) * LPW < 64, "ring depth");
     if (lo >= hi) return;
+    const int np = (hi - lo + 1) / 2;              // pairs
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = (int)threadIdx.x / DQ_THREADS, htid = (int)threadIdx.x % DQ_THREADS;
     const u32x4* seg = reinterpret_cast<const u32x4*>(seg_base);
-    auto issue = [&](int g) {
-        const int gb = g < hi ? g : hi - 1;
-        const u32x4* blk = seg + (size_t)gb * GC;
-        u32x4* slot = s.ring + (g % NR) * SLOT;
+    auto issue = [&](int j) {
+        const int jj = j < np ? j : np - 1;
+        const int first = lo + 2 * jj;
+        const int ncells = min(2, hi - first) * NC;   // the pair's cells inside the segment
+        const u32x4* blk = seg + (size_t)first * GC;
+        u32x4* slot = s.ring + (j % NR) * SLOT;
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const int c0 = (j * NWAVE + wave) * 64;    // this wavefront's 64 cells
-            const int c = min(c0 + lane, NC - 1);
+        for (int i = 0; i < LPW; ++i) {
+            const int c0 = (i * NWAVE + wave) * 64;    // this wavefront's 64 cells
+            const int c = min(c0 + lane, ncells - 1);
             __builtin_amdgcn_global_load_lds((glob_void*)(blk + c), (lds_void*)(slot + c0), 16, 0, 0);
         }
     };
+    auto dequant_pair = [&](int j) {
+        if (half == 0 || lo + 2 * j + 1 < hi)
+            dequant_block<D, BITS>(s.tile[j & 1][half], s.ring + (j % NR) * SLOT + half * NC, htid);
+    };
 #pragma unroll
-    for (int i = 0; i < NR; ++i) issue(lo + i);
-    __builtin_amdgcn_s_waitcnt(wait_vm((NR - 1) * LPW));      // this wavefront's part of block lo landed
+    for (int i = 0; i < NR; ++i) issue(i);
+    __builtin_amdgcn_s_waitcnt(wait_vm((NR - 1) * LPW));      // this wavefront's part of pair 0 landed
     lds_barrier();
-    dequant_block<D, BITS>(s.tile[lo & 1], s.ring + (lo % NR) * SLOT);
-    for (int g = lo; g < hi; ++g) {
-        __builtin_amdgcn_s_waitcnt(wait_vm((NR - 2) * LPW));  // ... of block g+1 (or its stand-in)
-        lds_barrier();           // block g dequantized, block g+1 landed, block g-1 consumed
-        issue(g + NR);           // into the slot of block g, dequantized one iteration ago
-        if (g + 1 < hi) dequant_block<D, BITS>(s.tile[(g + 1) & 1], s.ring + ((g + 1) % NR) * SLOT);
-        pf_block<D>(w, s.tile[g & 1], qscale, false, 0, qp, P);
+    dequant_pair(0);
+    for (int j = 0; j < np; ++j) {
+        __builtin_amdgcn_s_waitcnt(wait_vm((NR - 2) * LPW));  // ... of pair j+1 (or its stand-in)
+        lds_barrier();           // pair j dequantized, pair j+1 landed, pair j-1 consumed
+        issue(j + NR);           // into the slot of pair j, dequantized one iteration ago
+        if (j + 1 < np) dequant_pair(j + 1);
+        pf_block<D>(w, s.tile[j & 1][0], qscale, false, 0, qp, P);
+        if (lo + 2 * j + 1 < hi) pf_block<D>(w, s.tile[j & 1][1], qscale, false, 0, qp, P);
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));                     // the ring is reused by the next segment
     lds_barrier();
@@ -505,17 +519,17 @@ __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
                     ku = *reinterpret_cast<const uint4*>(kn + (size_t)tp * D + 8 * L);
                     vu = *reinterpret_cast<const uint4*>(vn + (size_t)tp * D + 8 * L);
                 }
-                *reinterpret_cast<uint4*>(&s.tile[0].k[t][8 * L]) = ku;
+                *reinterpret_cast<uint4*>(&s.tile[0][0].k[t][8 * L]) = ku;
                 const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int c0 = 8 * L + 2 * e, c1 = c0 + 1;
-                    vt_at(s.tile[0], c0, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] & 0xffffu));
-                    vt_at(s.tile[0], c1, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] >> 16));
+                    vt_at(s.tile[0][0], c0, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] & 0xffffu));
+                    vt_at(s.tile[0][0], c1, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] >> 16));
                 }
             }
             __syncthreads();
-            pf_block<D>(w, s.tile[0], p.qscale, true, 32 * nb, qp, p.P);
+            pf_block<D>(w, s.tile[0][0], p.qscale, true, 32 * nb, qp, p.P);
         }
     }
 
