@@ -143,42 +143,111 @@ def _pool_init():
 def _oracle_slice(args):
     """One (sequence, layer, KV head) slice through the oracle: quantize and
     pack every chunk at its bitwidth, dequantize, and attend with each query
-    head of the GQA group.  Returns (quantize s, attention s, algorithmic
-    attention bytes, tokens)."""
+    head of the GQA group.  The slice's arrays are read from a shared-memory
+    block (name, then (offset, shape, dtype) of k, v, q and the chunk
+    bitwidths).  Returns (quantize s, attention s, algorithmic attention
+    bytes, tokens)."""
     import numpy as np
+    from multiprocessing import shared_memory
     from chunk_mixed_precision_amd import configs
     from oracle import mkv_oracle as orc
-    kk, vv, qq, bits_row, C, d = args
-    n = len(bits_row)
-    t0 = time.perf_counter()
-    chunks = [orc.quantize_chunk(kk[c * C:(c + 1) * C], vv[c * C:(c + 1) * C], int(bits_row[c])) for c in range(n)]
-    t1 = time.perf_counter()
-    deq = [orc.dequant_chunk(ch) for ch in chunks]
-    kh = np.concatenate([x[0] for x in deq])
-    vh = np.concatenate([x[1] for x in deq])
-    for j in range(qq.shape[0]):
-        orc.attention(qq[j].astype(np.float64), kh, vh)
-    t2 = time.perf_counter()
-    nbytes = sum(configs.chunk_bytes(int(b), d, C) for b in bits_row) + qq.shape[0] * d * 6
+    from multiprocessing import resource_tracker
+    name, parts, C, d = args
+    shm = shared_memory.SharedMemory(name=name)
+    # attaching registers the block with the resource tracker as if this
+    # worker owned it (Python 3.10); the bench process creates and unlinks it
+    resource_tracker.unregister(shm._name, "shared_memory")
+    try:
+        kk, vv, qq, bits_row = (np.ndarray(shape, dtype=np.dtype(dt), buffer=shm.buf, offset=off)
+                                for off, shape, dt in parts)
+        n = len(bits_row)
+        t0 = time.perf_counter()
+        chunks = [orc.quantize_chunk(kk[c * C:(c + 1) * C], vv[c * C:(c + 1) * C], int(bits_row[c]))
+                  for c in range(n)]
+        t1 = time.perf_counter()
+        deq = [orc.dequant_chunk(ch) for ch in chunks]
+        kh = np.concatenate([x[0] for x in deq])
+        vh = np.concatenate([x[1] for x in deq])
+        for j in range(qq.shape[0]):
+            orc.attention(qq[j].astype(np.float64), kh, vh)
+        t2 = time.perf_counter()
+        nbytes = sum(configs.chunk_bytes(int(b), d, C) for b in bits_row) + qq.shape[0] * d * 6
+        del kk, vv, qq, bits_row, chunks, deq, kh, vh
+    finally:
+        shm.close()
     return t1 - t0, t2 - t1, nbytes, n * C
 
 
+def _share_slices(slices):
+    """Copy (k, v, q, bits, C, d) slices into one shared-memory block; returns
+    the block and one task argument per slice."""
+    shm, parts = _share_arrays([sl[:4] for sl in slices])
+    return shm, [(shm.name, p, sl[4], sl[5]) for p, sl in zip(parts, slices)]
+
+
 def _oracle_router(args):
-    """Oracle router logits (float64) for a block of tokens; returns seconds."""
+    """Oracle router logits (float64) for a block of tokens; returns seconds.
+    The block's bf16 hidden states, W12, W3 and b3 are read from a
+    shared-memory block (name, then their (offset, shape, dtype))."""
     import numpy as np
+    from multiprocessing import resource_tracker, shared_memory
     from oracle import mkv_oracle as orc
-    xb, w12b, w3, b3, inner = args
-    t0 = time.perf_counter()
-    orc.router_logits(orc.bf16_bits_to_f64(xb), orc.bf16_bits_to_f64(w12b), w3, b3, inner)
-    return time.perf_counter() - t0
+    name, parts, inner = args
+    shm = shared_memory.SharedMemory(name=name)
+    resource_tracker.unregister(shm._name, "shared_memory")
+    try:
+        xb, w12b, w3, b3 = (np.ndarray(shape, dtype=np.dtype(dt), buffer=shm.buf, offset=off)
+                            for off, shape, dt in parts)
+        t0 = time.perf_counter()
+        orc.router_logits(orc.bf16_bits_to_f64(xb), orc.bf16_bits_to_f64(w12b), w3, b3, inner)
+        dt = time.perf_counter() - t0
+        del xb, w12b, w3, b3
+    finally:
+        shm.close()
+    return dt
+
+
+def _share_arrays(groups):
+    """Copy groups of arrays into one shared-memory block; returns the block
+    and, per group, the (offset, shape, dtype) of its arrays."""
+    import numpy as np
+    from multiprocessing import shared_memory
+    total = sum(a.nbytes + 64 for g in groups for a in g)
+    shm = shared_memory.SharedMemory(create=True, size=max(total, 1))
+    out = []
+    off = 0
+    for g in groups:
+        parts = []
+        for a in g:
+            a = np.ascontiguousarray(a)
+            np.ndarray(a.shape, dtype=a.dtype, buffer=shm.buf, offset=off)[...] = a
+            parts.append((off, a.shape, a.dtype.str))
+            off += (a.nbytes + 63) // 64 * 64
+        out.append(tuple(parts))
+    return shm, out
 
 
 def make_cpu_pool():
-    """Worker processes for the oracle timing, forked before this process
-    touches the GPU (the workers run numpy only)."""
+    """Worker processes for the oracle timing, started before this process
+    touches the GPU.  They are spawned (a fresh interpreter each) with every
+    BLAS/OpenMP thread count set to 1 in their environment, so that each
+    worker computes on one thread from its first numpy call, whatever
+    threading the host's numpy would otherwise set up."""
     import multiprocessing as mp
     n = _cpu_threads()
-    return mp.get_context("fork").Pool(n, initializer=_pool_init), n
+    keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS",
+            "NUMEXPR_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in keys}
+    os.environ.update({k: "1" for k in keys})
+    try:
+        pool = mp.get_context("spawn").Pool(n, initializer=_pool_init)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return pool, n
 
 
 def cpu_baseline(pool, ncores, wl, budget_s):
@@ -190,11 +259,20 @@ def cpu_baseline(pool, ncores, wl, budget_s):
     workers the host actually gives this process (the CPU share of a shared
     box need not show in its affinity mask), and the rest of the budget of
     about `budget_s` seconds of task time runs at the fastest width.  The
-    slices are copied to the host before any timing; every width is timed
-    by the wall clock around its wave.  For
-    routed workloads the oracle router also runs on blocks of 256 tokens."""
+    slices are copied to a shared-memory block before any timing (a task
+    passes only its offsets); every width is timed by the wall clock around
+    its wave.  For routed workloads the oracle router also runs on blocks of
+    256 tokens."""
     gen = wl.cpu_slices()
-    distinct = [next(gen) for _ in range(min(wl.w.Hkv, 8))]     # copied to the host before any timing
+    shm, distinct = _share_slices([next(gen) for _ in range(min(wl.w.Hkv, 8))])   # on the host before any timing
+    try:
+        return _cpu_baseline_runs(pool, ncores, wl, budget_s, distinct)
+    finally:
+        shm.close()
+        shm.unlink()
+
+
+def _cpu_baseline_runs(pool, ncores, wl, budget_s, distinct):
     count = [0]
 
     def take(k):
@@ -251,10 +329,16 @@ def cpu_baseline(pool, ncores, wl, budget_s):
     if rt is not None:
         blocks, flop_per_block = rt
         blocks = blocks[:best_k]
-        solo_r = pool.apply(_oracle_router, (blocks[0],))
-        t0 = time.perf_counter()
-        pool.map(_oracle_router, blocks, chunksize=1)
-        rwall = time.perf_counter() - t0
+        shm, parts = _share_arrays([b[:4] for b in blocks])
+        try:
+            tasks = [(shm.name, p, b[4]) for p, b in zip(parts, blocks)]
+            solo_r = pool.apply(_oracle_router, (tasks[0],))
+            t0 = time.perf_counter()
+            pool.map(_oracle_router, tasks, chunksize=1)
+            rwall = time.perf_counter() - t0
+        finally:
+            shm.close()
+            shm.unlink()
         out["router_tflops"] = round(len(blocks) * flop_per_block / rwall / 1e12, 5)
         out["router_tflops_one_thread"] = round(flop_per_block / solo_r / 1e12, 5)
         sample += f"; router: {len(blocks)} blocks of 256 tokens in float64 side by side ({rwall:.1f} s wall)"
@@ -608,7 +692,7 @@ def main():
               "(pass --gpus 1; sharding is described in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
 
-    # the oracle's worker processes are forked before anything touches the GPU
+    # the oracle's worker processes start before anything touches the GPU
     pool, ncores = make_cpu_pool() if args.cpu_seconds > 0 else (None, 0)
 
     import numpy as np
