@@ -10,6 +10,10 @@
 #include "mkv_internal.h"
 #include "mkv_kernels.h"
 
+namespace mkv {
+int prefill_query_tile(int P);   // queries per prefill workgroup (defined with the kernels)
+}
+
 namespace {
 
 thread_local int g_last_hip = 0;
@@ -42,15 +46,23 @@ inline int attn_workgroups(int B, int Hkv, int d, const int* cap, int C) {
 }
 
 // Chunked prefill: splits of each (sequence, query head)'s cached group
-// blocks, enough that the grid covers about one 8-wavefront workgroup per CU,
-// none shorter than 4 group blocks (counted at capacity).
+// blocks.  One 8-wavefront workgroup fits a CU at a time, so the grid runs in
+// rounds of 256: take at least enough splits for one round, and more while
+// the last round would be less than 90 % full; none shorter than 4 group
+// blocks (counted at capacity), at most 32.
 inline int prefill_splits(int B, int Hq, int P, const int* cap, int C) {
-    const long long tiles = (long long)B * Hq * ((P + 255) / 256);
-    long long ns = (256 + tiles - 1) / tiles;
+    const int qt = mkv::prefill_query_tile(P);
+    const long long tiles = (long long)B * Hq * ((P + qt - 1) / qt);
     const long long gcap = ((long long)cap[0] + cap[1] + cap[2]) * (C / mkv::kGroup);
-    if (ns > gcap / 4) ns = gcap / 4;
-    if (ns > 32) ns = 32;
-    if (ns < 1) ns = 1;
+    long long lim = gcap / 4 < 32 ? gcap / 4 : 32;
+    if (lim < 1) lim = 1;
+    long long ns = (256 + tiles - 1) / tiles;
+    if (ns > lim) ns = lim;
+    while (ns < lim) {
+        const long long wg = tiles * ns, rounds = (wg + 255) / 256;
+        if (wg * 10 >= rounds * 256 * 9) break;
+        ++ns;
+    }
     return (int)ns;
 }
 

@@ -6,7 +6,10 @@
 //
 // Unlike a decode step this is a dense contraction (P queries x T tokens x
 // d), so it runs on the matrix cores.  A workgroup holds 256 queries of one
-// query head (32 per wavefront) and one split of the cached group blocks.
+// query head (32 per wavefront) and one split of the cached group blocks;
+// with at most 128 queries it holds 128, and its two halves of four
+// wavefronts take alternate group blocks, their softmax states merged in LDS
+// at the end.
 // Each 32-token group block is dequantized once into LDS as fp16 -- keys
 // token-major, values channel-major -- and shared by the eight wavefronts;
 // each wavefront then computes S^T = K Q^T with v_mfma_f32_32x32x16_f16
@@ -28,7 +31,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // a 16-byte cell 
 constexpr int NWAVE = 8;                // wavefronts per workgroup (2 per SIMD)
 constexpr int PT = 64 * NWAVE;          // threads per workgroup
 constexpr int QPW = 32;                 // queries per wavefront
-constexpr int QT = QPW * NWAVE;         // queries per workgroup
+constexpr int QT = QPW * NWAVE;         // queries per workgroup (256)
+constexpr int QT_HALF = QT / 2;         // queries per workgroup when P <= 128
 constexpr int RING_CELLS = 4096;        // 64 KB ring of raw group-block pairs (16-byte cells)
 constexpr int DQ_THREADS = PT / 2;      // threads that dequantize one group block of a pair
 
@@ -397,8 +401,9 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, floa
 // pair j from the other, with one barrier between iterations: the barrier,
 // the ring traffic and the dequant latency are paid once per 64 tokens.
 // A pair whose second block lies past hi (an odd count) has only its first
-// block dequantized and attended.
-template <int D, int BITS>
+// block dequantized and attended.  With HALF, wavefronts 0-3 attend the first
+// block of each pair and wavefronts 4-7 the second.
+template <int D, int BITS, bool HALF>
 __device__ __forceinline__ void pf_segment(PfState<D>& w, PfLds<D>& s, const uint8_t* seg_base, int lo, int hi,
                                            float qscale, int qp, int P) {
     constexpr int S = D / 8;
@@ -440,8 +445,13 @@ __device__ __forceinline__ void pf_segment(PfState<D>& w, PfLds<D>& s, const uin
         lds_barrier();           // pair j dequantized, pair j+1 landed, pair j-1 consumed
         issue(j + NR);           // into the slot of pair j, dequantized one iteration ago
         if (j + 1 < np) dequant_pair(j + 1);
-        pf_block<D>(w, s.tile[j & 1][0], qscale, false, 0, qp, P);
-        if (lo + 2 * j + 1 < hi) pf_block<D>(w, s.tile[j & 1][1], qscale, false, 0, qp, P);
+        if constexpr (HALF) {
+            const int bh = __builtin_amdgcn_readfirstlane(wave) >> 2;
+            if (bh == 0 || lo + 2 * j + 1 < hi) pf_block<D>(w, s.tile[j & 1][bh], qscale, false, 0, qp, P);
+        } else {
+            pf_block<D>(w, s.tile[j & 1][0], qscale, false, 0, qp, P);
+            if (lo + 2 * j + 1 < hi) pf_block<D>(w, s.tile[j & 1][1], qscale, false, 0, qp, P);
+        }
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));                     // the ring is reused by the next segment
     lds_barrier();
@@ -449,18 +459,22 @@ __device__ __forceinline__ void pf_segment(PfState<D>& w, PfLds<D>& s, const uin
 
 }  // namespace
 
-// grid: x = query tile (QT queries), y = split, z = sequence * Hq + query head
-template <int D>
+// grid: x = query tile (QT, or QT_HALF with HALF, queries), y = split,
+// z = sequence * Hq + query head
+template <int D, bool HALF>
 __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
     __shared__ __align__(16) PfLds<D> s;
     constexpr int S = D / 8;
+    constexpr int QW = HALF ? NWAVE / 2 : NWAVE;     // wavefronts per set of queries
+    constexpr int QTK = QPW * QW;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int lh = lane >> 5;
     const int qtile = blockIdx.x, split = blockIdx.y;
     const int bq = blockIdx.z, b = bq / p.Hq, hq = bq % p.Hq;
     const int h = hq / (p.Hq / p.Hkv);
     const int bh = b * p.Hkv + h;
-    const int qp = qtile * QT + wave * QPW + (lane & 31);   // this lane's query position
+    const int qp = qtile * QTK + (wave % QW) * QPW + (lane & 31);   // this lane's query position
     const bool qvalid = qp < p.P;
 
     PfState<D> w;
@@ -493,44 +507,81 @@ __global__ __launch_bounds__(PT) void prefill_tile_kernel(PrefillParams p) {
     const int g0 = (int)((long long)split * W / p.NS), g1 = (int)((long long)(split + 1) * W / p.NS);
     {
         int base = 0;
-        pf_segment<D, 16>(w, s, p.pool[0] + (size_t)bh * p.cap[0] * gpc * group_bytes(16, D),
-                          max(g0 - base, 0), min(g1 - base, segg[0]), p.qscale, qp, p.P);
+        pf_segment<D, 16, HALF>(w, s, p.pool[0] + (size_t)bh * p.cap[0] * gpc * group_bytes(16, D),
+                                max(g0 - base, 0), min(g1 - base, segg[0]), p.qscale, qp, p.P);
         base += segg[0];
-        pf_segment<D, 4>(w, s, p.pool[1] + (size_t)bh * p.cap[1] * gpc * group_bytes(4, D),
-                         max(g0 - base, 0), min(g1 - base, segg[1]), p.qscale, qp, p.P);
+        pf_segment<D, 4, HALF>(w, s, p.pool[1] + (size_t)bh * p.cap[1] * gpc * group_bytes(4, D),
+                               max(g0 - base, 0), min(g1 - base, segg[1]), p.qscale, qp, p.P);
         base += segg[1];
-        pf_segment<D, 2>(w, s, p.pool[2] + (size_t)bh * p.cap[2] * gpc * group_bytes(2, D),
-                         max(g0 - base, 0), min(g1 - base, segg[2]), p.qscale, qp, p.P);
+        pf_segment<D, 2, HALF>(w, s, p.pool[2] + (size_t)bh * p.cap[2] * gpc * group_bytes(2, D),
+                               max(g0 - base, 0), min(g1 - base, segg[2]), p.qscale, qp, p.P);
     }
 
     // ---------------- this split's blocks of the new chunk's own tokens, causal
+    // (two at a time with HALF: one per half of the workgroup)
     {
         // blocks past this tile's last query see nothing
-        const int last = min(nblk, (qtile * QT + QT + 31) / 32);
+        const int last = min(nblk, (qtile * QTK + QTK + 31) / 32);
         const int nb0 = max(g0 - total, 0), nb1 = min(g1 - total, last);
         const uint16_t* kn = p.k_new + (size_t)bh * p.P * D;
         const uint16_t* vn = p.v_new + (size_t)bh * p.P * D;
-        for (int nb = nb0; nb < nb1; ++nb) {
+        constexpr int NBI = HALF ? 2 : 1;           // blocks per iteration
+        for (int nb = nb0; nb < nb1; nb += NBI) {
+            const int nload = min(NBI, nb1 - nb);
             __syncthreads();
-            for (int c = tid; c < 32 * S; c += PT) {
-                const int t = c / S, L = c % S, tp = 32 * nb + t;
+            for (int c = tid; c < nload * 32 * S; c += PT) {
+                const int bi = c / (32 * S), t = (c / S) % 32, L = c % S, tp = 32 * (nb + bi) + t;
+                PfTile<D>& tl = s.tile[0][bi];
                 uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
                 if (tp < p.P) {
                     ku = *reinterpret_cast<const uint4*>(kn + (size_t)tp * D + 8 * L);
                     vu = *reinterpret_cast<const uint4*>(vn + (size_t)tp * D + 8 * L);
                 }
-                *reinterpret_cast<uint4*>(&s.tile[0][0].k[t][8 * L]) = ku;
+                *reinterpret_cast<uint4*>(&tl.k[t][8 * L]) = ku;
                 const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int c0 = 8 * L + 2 * e, c1 = c0 + 1;
-                    vt_at(s.tile[0][0], c0, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] & 0xffffu));
-                    vt_at(s.tile[0][0], c1, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] >> 16));
+                    vt_at(tl, c0, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] & 0xffffu));
+                    vt_at(tl, c1, t >> 2)[t & 3] = __builtin_bit_cast(_Float16, (uint16_t)(vw[e] >> 16));
                 }
             }
             __syncthreads();
-            pf_block<D>(w, s.tile[0][0], p.qscale, true, 32 * nb, qp, p.P);
+            const int bi = HALF ? (wave_u >> 2) : 0;
+            if (bi < nload) pf_block<D>(w, s.tile[0][bi], p.qscale, true, 32 * (nb + bi), qp, p.P);
         }
+    }
+
+    // ---------------- HALF: the second half's state merged into the first's
+    // (the same log-sum-exp merge as the combine), through LDS laid out
+    // [value][wavefront][lane]; the second half then has nothing left to do
+    if constexpr (HALF) {
+        constexpr int NO = D / 2;                   // accumulator values per lane
+        static_assert((NO + 2) * 4 * 64 * sizeof(float) <= sizeof(PfLds<D>), "merge area");
+        float* xs = reinterpret_cast<float*>(&s);
+        const int wq = wave_u & 3;
+        auto at = [&](int k) { return xs + ((size_t)k * 4 + wq) * 64 + lane; };
+        __syncthreads();                            // every wavefront is done with the tiles
+        if (wave_u >= 4) {
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) *at(16 * t + r) = w.o[t][r];
+            *at(NO) = w.m;
+            *at(NO + 1) = w.l;
+        }
+        __syncthreads();
+        if (wave_u >= 4) return;
+        const float m2 = *at(NO), l2 = *at(NO + 1);
+        const float mx = fmaxf(w.m, m2);
+        const float a1 = (w.m == -INFINITY) ? 0.f : exp2_fast(w.m - mx);
+        const float a2 = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - mx);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w.o[t][r] = __builtin_fmaf(*at(16 * t + r), a2, w.o[t][r] * a1);
+        w.l = __builtin_fmaf(l2, a2, w.l * a1);
+        w.m = mx;
     }
 
     // ---------------- partial record of this split: o (unnormalised), m, l
@@ -602,15 +653,21 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillParams p) {
     for (int c = 0; c < PL; ++c) out[c] = acc[c] * inv;
 }
 
+int prefill_query_tile(int P) { return P <= QT_HALF ? QT_HALF : QT; }
+
 hipError_t launch_prefill(const PrefillParams& pp, int D, hipStream_t st) {
-    const dim3 grid((pp.P + QT - 1) / QT, pp.NS, pp.B * pp.Hq);
+    const int qt = prefill_query_tile(pp.P);
+    const bool half = qt == QT_HALF;
+    const dim3 grid((pp.P + qt - 1) / qt, pp.NS, pp.B * pp.Hq);
     const size_t rows = (size_t)pp.B * pp.Hq * pp.P;
     const dim3 cgrid((unsigned)((rows + 3) / 4));
     if (D == 128) {
-        prefill_tile_kernel<128><<<grid, PT, 0, st>>>(pp);
+        if (half) prefill_tile_kernel<128, true><<<grid, PT, 0, st>>>(pp);
+        else prefill_tile_kernel<128, false><<<grid, PT, 0, st>>>(pp);
         prefill_combine_kernel<128><<<cgrid, 256, 0, st>>>(pp);
     } else if (D == 64) {
-        prefill_tile_kernel<64><<<grid, PT, 0, st>>>(pp);
+        if (half) prefill_tile_kernel<64, true><<<grid, PT, 0, st>>>(pp);
+        else prefill_tile_kernel<64, false><<<grid, PT, 0, st>>>(pp);
         prefill_combine_kernel<64><<<cgrid, 256, 0, st>>>(pp);
     } else {
         return hipErrorInvalidValue;

@@ -114,3 +114,19 @@ def test_prefill_attention_full_size_llama2_7b_32k_sampled():
     rows = [0, 1, 31, 32, 127, 128, 200, 255]
     err = check_prefill(w, tab, cache, q, kn, vn, out, heads, rows)
     note(f"  max rel err {err:.2e} over {len(heads) * len(rows)} sampled query rows")
+
+
+def test_prefill_attention_full_size_llama2_13b_sampled():
+    """The llama2-13b shape (16 sequences, 40 heads, 8192 cached tokens at
+    chunk 128) with a 128-token chunk: the 128-query workgroups whose two
+    halves take alternate group blocks; sampled sequences, heads and rows."""
+    w = configs.Workload(name="prefill-13b-8k", seed=83, B=16, Hq=40, Hkv=40, d=128, T=8192, C=128,
+                         mix=(0.05, 0.75, 0.20), outlier_cols=100, outlier_mult=8.0)
+    note(f"prefill {w.name}, P=128")
+    experts = synth.drawn_chunk_experts(w)
+    tab, cache, q, kn, vn, out = run_prefill(w, experts, 128)
+    rng = np.random.default_rng(4)
+    heads = [(int(b), int(hq)) for b, hq in zip(rng.choice(16, 6), rng.choice(40, 6))] + [(15, 39)]
+    rows = [0, 1, 31, 32, 63, 64, 100, 127]
+    err = check_prefill(w, tab, cache, q, kn, vn, out, heads, rows)
+    note(f"  max rel err {err:.2e} over {len(heads) * len(rows)} sampled query rows")
