@@ -56,6 +56,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Largest rise of the softmax maximum (log2 units) absorbed without moving
+// the reference point: probabilities reach at most 2^8 before fp16 rounding.
+constexpr float kSlack = 8.f;
+
 // The value of lane l ^ 32.  v_permlane32_swap exchanges the upper half of
 // one register with the lower half of another; applied to two copies of x,
 // lanes 0-31 of the second copy and lanes 32-63 of the first then hold the
@@ -360,8 +364,14 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, floa
         mloc = fmaxf(mloc, x);
     }
     mloc = fmaxf(mloc, swap_halves(mloc)) * qscale;     // with the query's other tokens
-    const float mn = fmaxf(w.m, mloc);
-    const float alpha = (mn == -INFINITY) ? 1.f : exp2_fast(w.m - mn);
+    // The reference point m moves only when the block's maximum exceeds it by
+    // more than kSlack (log2 units): probabilities then stay below 2^kSlack,
+    // far inside fp16 and fp32 range, and o and l carry the same factor, so
+    // o / l is unchanged while the rescale of o becomes rare.  The first
+    // visible token always moves m off -inf (alpha = exp2(-inf) = 0).
+    const bool raise = mloc > w.m + kSlack;
+    const float mn = raise ? mloc : w.m;
+    const float alpha = raise ? exp2_fast(w.m - mn) : 1.f;
     // a lane with no visible token yet (mn = -inf) has only -inf scores,
     // which the reference 0 sends to exp2(-inf) = 0
     const float mref = (mn == -INFINITY) ? 0.f : mn;
@@ -376,9 +386,7 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, floa
     }
     w.l = __builtin_fmaf(w.l, alpha, ps);
     w.m = mn;
-    // the running max rarely rises after the first blocks: rescale only then
-    // (alpha is exactly 1 for a lane whose max stayed)
-    if (__ballot(alpha != 1.f)) {
+    if (__ballot(raise)) {
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -417,6 +425,7 @@ __device__ __forceinline__ void pf_segment(PfState<D>& w, PfLds<D>& s, const uin
     const int np = (hi - lo + 1) / 2;              // pairs
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = (int)threadIdx.x / DQ_THREADS, htid = (int)threadIdx.x % DQ_THREADS;
+    const int grp = __builtin_amdgcn_readfirstlane(wave) >> 2;     // wavefronts 0-3 or 4-7
     const u32x4* seg = reinterpret_cast<const u32x4*>(seg_base);
     auto issue = [&](int j) {
         const int jj = j < np ? j : np - 1;
@@ -444,14 +453,18 @@ __device__ __forceinline__ void pf_segment(PfState<D>& w, PfLds<D>& s, const uin
         __builtin_amdgcn_s_waitcnt(wait_vm((NR - 2) * LPW));  // ... of pair j+1 (or its stand-in)
         lds_barrier();           // pair j dequantized, pair j+1 landed, pair j-1 consumed
         issue(j + NR);           // into the slot of pair j, dequantized one iteration ago
-        if (j + 1 < np) dequant_pair(j + 1);
+        // Wavefronts 0-3 dequantize before they compute, 4-7 after: the two
+        // wavefronts of each SIMD then run opposite phases (one on the vector
+        // unit while the other feeds the matrix core).
+        const bool dq_first = grp == 0;
+        if (dq_first && j + 1 < np) dequant_pair(j + 1);
         if constexpr (HALF) {
-            const int bh = __builtin_amdgcn_readfirstlane(wave) >> 2;
-            if (bh == 0 || lo + 2 * j + 1 < hi) pf_block<D>(w, s.tile[j & 1][bh], qscale, false, 0, qp, P);
+            if (grp == 0 || lo + 2 * j + 1 < hi) pf_block<D>(w, s.tile[j & 1][grp], qscale, false, 0, qp, P);
         } else {
             pf_block<D>(w, s.tile[j & 1][0], qscale, false, 0, qp, P);
             if (lo + 2 * j + 1 < hi) pf_block<D>(w, s.tile[j & 1][1], qscale, false, 0, qp, P);
         }
+        if (!dq_first && j + 1 < np) dequant_pair(j + 1);
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));                     // the ring is reused by the next segment
     lds_barrier();
