@@ -25,6 +25,7 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // a 16-byte cell as a value type
 
@@ -375,15 +376,23 @@ __device__ __forceinline__ void pf_block(PfState<D>& w, const PfTile<D>& s, floa
     // a lane with no visible token yet (mn = -inf) has only -inf scores,
     // which the reference 0 sends to exp2(-inf) = 0
     const float mref = (mn == -INFINITY) ? 0.f : mn;
-    float ps = 0.f;
     f16x8 pf0, pf1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const float pr = exp2_fast(__builtin_fmaf(st[r], qscale, -mref));
-        ps += pr;
         if (r < 8) pf0[r] = (_Float16)pr;
         else pf1[r - 8] = (_Float16)pr;
     }
+    // the denominator sums the fp16 probabilities that weight the values,
+    // two per v_dot2_f32_f16 (products by 1 are exact, the sum is fp32)
+    float ps = 0.f, ps1 = 0.f;
+    const h2_t one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ps = __builtin_amdgcn_fdot2(h2_t{pf0[2 * i], pf0[2 * i + 1]}, one, ps, false);
+        ps1 = __builtin_amdgcn_fdot2(h2_t{pf1[2 * i], pf1[2 * i + 1]}, one, ps1, false);
+    }
+    ps += ps1;
     w.l = __builtin_fmaf(w.l, alpha, ps);
     w.m = mn;
     if (__ballot(raise)) {
