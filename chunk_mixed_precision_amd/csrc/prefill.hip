@@ -9,13 +9,12 @@
 // query head (32 per wavefront) and one split of the cached group blocks;
 // with at most 128 queries it holds 128, and its two halves of four
 // wavefronts take alternate group blocks, their softmax states merged in LDS
-// at the end.
-// Each 32-token group block is dequantized once into LDS as fp16 -- keys
-// token-major, values channel-major -- and shared by the eight wavefronts;
-// each wavefront then computes S^T = K Q^T with v_mfma_f32_32x32x16_f16
-// (lane = query, so the online softmax is lane-local), and O^T += V^T P^T
-// with the probabilities fed from its own accumulator registers.  Splits are
-// merged by a log-sum-exp combine.
+// at the end.  Each 32-token group block is dequantized once into LDS as
+// fp16 -- keys token-major, values channel-major -- and shared by the
+// wavefronts; each wavefront then computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_f16 (lane = query, so the online softmax is
+// lane-local), and O^T += V^T P^T with the probabilities made from its own
+// score registers.  Splits are merged by a log-sum-exp combine.
 #include "mkv_internal.h"
 #include "mkv_kernels.h"
 

@@ -130,3 +130,18 @@ def test_prefill_attention_full_size_llama2_13b_sampled():
     rows = [0, 1, 31, 32, 63, 64, 100, 127]
     err = check_prefill(w, tab, cache, q, kn, vn, out, heads, rows)
     note(f"  max rel err {err:.2e} over {len(heads) * len(rows)} sampled query rows")
+
+
+def test_prefill_attention_is_deterministic():
+    """The prefill's splits and block order are fixed by the shapes (no work
+    tickets), so two calls on the same inputs agree bit for bit, in both
+    workgroup modes (P <= 128 and P > 128)."""
+    w = configs.Workload(name="prefill-repeat", seed=91, B=2, Hq=8, Hkv=2, d=128, T=2048, C=128,
+                         mix=(0.2, 0.4, 0.4), outlier_cols=3, outlier_mult=8.0)
+    experts = synth.drawn_chunk_experts(w)
+    for Pn in (100, 200):
+        tab, cache, q, kn, vn, out = run_prefill(w, experts, Pn)
+        again = mkv.mixed_kv_prefill_attention(q, cache, kn, vn)
+        torch.cuda.synchronize()
+        assert torch.equal(out, again), f"prefill differs between calls at P={Pn}"
+        note(f"  P={Pn}: bit-identical over {out.numel()} outputs")
