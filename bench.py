@@ -704,8 +704,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(pass --gpus 1; sharding is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path; run it with --gpus 1 "
+              "(each GPU would hold whole (sequence, KV head) streams of its own)", file=sys.stderr)
         sys.exit(2)
 
     # the oracle's worker processes start before anything touches the GPU

@@ -21,8 +21,7 @@ in IEEE float32, one rounded operation at a time (numpy float32 element-wise
 arithmetic never contracts a*b+c into an FMA), because the codes, scales and
 minima must be reproduced bit for bit.
 
-Readings taken where the pages are silent or garbled (each one also listed in
-the design notes):
+Readings taken where the pages are silent or garbled:
   R1  The router formula on the MoQAE page lost its operators in extraction.
       It is read as z = f((X W1^T) * (X W2^T)) W3^T + b3 with "*" the
       element-wise product and f = SiLU applied to that product.  Only the
