@@ -110,8 +110,10 @@ __device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
 
 // Two fp16 results packed in one word: low = fp16(ya.h * wa + oa), high =
 // fp16(yb.h * wb + ob), where .h is the low (HSEL 0) or high (HSEL 1) fp16
-// half of ya / yb, and the products and sums are formed in fp32
-// (v_fma_mixlo_f16 / v_fma_mixhi_f16).
+// half of ya / yb.  Each product and sum is one fused fp32 operation on the
+// fp16 input (v_fma_mix_f32), and one v_cvt_pk_f16_f32 rounds both to fp16:
+// on this part that issues faster than writing each half with
+// v_fma_mixlo_f16 / v_fma_mixhi_f16 (which round straight to fp16).
 // f(integral_constant<int, 0>{}), ..., f(integral_constant<int, N-1>{})
 template <int N, int I = 0, class Fn>
 __device__ __forceinline__ void static_for(Fn&& fn) {
@@ -123,16 +125,10 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 
 template <int HSEL>
 __device__ __forceinline__ uint32_t mix_pair(uint32_t ya, uint32_t yb, float wa, float oa, float wb, float ob) {
-    uint32_t d;
-    if constexpr (HSEL == 0)
-        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]\n\t"
-            "v_fma_mixhi_f16 %0, %4, %5, %6 op_sel_hi:[1,0,0]"
-            : "=&v"(d) : "v"(ya), "v"(wa), "v"(oa), "v"(yb), "v"(wb), "v"(ob));
-    else
-        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
-            "v_fma_mixhi_f16 %0, %4, %5, %6 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-            : "=&v"(d) : "v"(ya), "v"(wa), "v"(oa), "v"(yb), "v"(wb), "v"(ob));
-    return d;
+    const h2_t ha = __builtin_bit_cast(h2_t, ya), hb = __builtin_bit_cast(h2_t, yb);
+    const float fa = __builtin_fmaf((float)ha[HSEL], wa, oa);
+    const float fb = __builtin_fmaf((float)hb[HSEL], wb, ob);
+    return __builtin_bit_cast(uint32_t, h2_t{(_Float16)fa, (_Float16)fb});
 }
 
 // Packed group block (raw, 16-byte cells as laid out in the pool) -> fp16
