@@ -418,6 +418,12 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     // the weight, so the fp32 accumulators lose at most a few bits.
     uint32_t vmagic;
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(vmagic));
+    // With two query heads per row the INT4 codes are instead unpacked into
+    // bytes and converted to fp32 (v_cvt_f32_ubyte), once for both heads,
+    // and multiplied with plain fp32 FMAs, which issue faster than the mixed
+    // fp16/fp32 ones; the weights then carry no 1/16 and the accumulators no
+    // pattern offset.
+    constexpr bool CVT4 = HPR == 2;
     auto lo16 = [](uint32_t y) { return (float)__builtin_bit_cast(half2_t, y).x; };
     auto hi16 = [](uint32_t y) { return (float)__builtin_bit_cast(half2_t, y).y; };
 
@@ -477,7 +483,8 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     };
 
     // ---- INT-b pieces
-    auto key_meta = [&](const uint4* m4) {           // rows: scale lo, scale hi, min lo, min hi
+    auto key_meta = [&](const uint4* m4, auto cvt_tag) {   // rows: scale lo, scale hi, min lo, min hi
+        constexpr bool CVT = decltype(cvt_tag)::value;
         const float4 s0 = as_f4(m4[0]), s1 = as_f4(m4[1]), n0 = as_f4(m4[2]), n1 = as_f4(m4[3]);
         const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         const float kmn[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
@@ -487,11 +494,15 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 bias = __builtin_fmaf(qs[j][e], kmn[e], bias);
-                kw[j][e] = qs[j][e] * ks[e] * 0.0625f;
+                kw[j][e] = CVT ? qs[j][e] * ks[e] : qs[j][e] * ks[e] * 0.0625f;
                 sw += kw[j][e];
             }
-            koff[j] = __builtin_fmaf(-1024.f, sw, bias);
-            koff64[j] = __builtin_fmaf(-256.f, sw, bias);
+            if constexpr (CVT) {
+                koff[j] = bias;
+            } else {
+                koff[j] = __builtin_fmaf(-1024.f, sw, bias);
+                koff64[j] = __builtin_fmaf(-256.f, sw, bias);
+            }
         }
     };
     // 4 key-code rows of one half (INT4).  Field f of word w is the code of
@@ -502,6 +513,27 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
         for (int j = 0; j < HPR; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][r] = koff[j];
+        if constexpr (CVT4) {
+            // field g of a word: byte g/2 of its low (g even) or high (g odd) nibbles
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int w = i >> 1;
+                const uint32_t ws[4] = {rows[i].x, rows[i].y, rows[i].z, rows[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = ws[e] & 0x0F0F0F0Fu, hi = (ws[e] >> 4) & 0x0F0F0F0Fu;
+                    const float c[8] = {cvt_ub<0>(lo), cvt_ub<0>(hi), cvt_ub<1>(lo), cvt_ub<1>(hi),
+                                        cvt_ub<2>(lo), cvt_ub<2>(hi), cvt_ub<3>(lo), cvt_ub<3>(hi)};
+#pragma unroll
+                    for (int j = 0; j < HPR; ++j) {
+                        const float wq = kw[j][4 * (i & 1) + e];
+#pragma unroll
+                        for (int g = 0; g < 8; ++g) acc[j][8 * w + g] = __builtin_fmaf(wq, c[g], acc[j][8 * w + g]);
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int w = i >> 1;
@@ -562,7 +594,8 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
             for (int i = 0; i < NTH; ++i) sc[j][hh * NTH + i] = acc[j][i];
         }
     };
-    auto value_meta = [&](const uint4* m4) {         // (scale, min) of tokens t_{2r}, t_{2r+1}
+    auto value_meta = [&](const uint4* m4, auto cvt_tag) {   // (scale, min) of tokens t_{2r}, t_{2r+1}
+        constexpr bool CVT = decltype(cvt_tag)::value;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const float4 sm = as_f4(m4[m >> 1]);
@@ -571,12 +604,35 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
 #pragma unroll
             for (int j = 0; j < HPR; ++j) {
                 pm[j] = __builtin_fmaf(pw[j][m], mn, pm[j]);
-                pw[j][m] = pw[j][m] * s * 0.0625f;
+                pw[j][m] = CVT ? pw[j][m] * s : pw[j][m] * s * 0.0625f;
             }
         }
     };
     // row m: token tq + 4m; word u holds channels 8u .. 8u+7 of the group
     auto values_int4 = [&](const uint4* rows) {
+        if constexpr (CVT4) {
+#pragma unroll
+            for (int j = 0; j < HPR; ++j)
+#pragma unroll
+                for (int c = 0; c < 32; ++c) o[j][c] *= alpha_v[j];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const uint32_t ws[4] = {rows[m].x, rows[m].y, rows[m].z, rows[m].w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t lo = ws[u] & 0x0F0F0F0Fu, hi = (ws[u] >> 4) & 0x0F0F0F0Fu;
+                    const float c[8] = {cvt_ub<0>(lo), cvt_ub<0>(hi), cvt_ub<1>(lo), cvt_ub<1>(hi),
+                                        cvt_ub<2>(lo), cvt_ub<2>(hi), cvt_ub<3>(lo), cvt_ub<3>(hi)};
+#pragma unroll
+                    for (int j = 0; j < HPR; ++j) {
+                        const float wv = pw[j][m];
+#pragma unroll
+                        for (int g = 0; g < 8; ++g) o[j][8 * u + g] = __builtin_fmaf(wv, c[g], o[j][8 * u + g]);
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < HPR; ++j) {
             float sw = 0.f;
@@ -679,27 +735,27 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
         constexpr int BITS = decltype(bits_tag)::value;
         if constexpr (BITS == 4) {
             if (ph == 0) {
-                key_meta(cur);
+                key_meta(cur, std::integral_constant<bool, CVT4>{});
                 key_half_int4(cur + 4);
                 take_half(0);
             } else if (ph == 1) {
                 key_half_int4(cur);
                 take_half(1);
                 softmax_step(bits_tag, valid);
-                value_meta(cur + 4);
+                value_meta(cur + 4, std::integral_constant<bool, CVT4>{});
             } else {
                 values_int4(cur);
             }
         } else if constexpr (BITS == 2) {
             if (ph == 0) {
-                key_meta(cur);
+                key_meta(cur, std::false_type{});
                 key_half_int2(cur + 4);
                 take_half(0);
                 key_half_int2(cur + 6);
                 take_half(1);
                 softmax_step(bits_tag, valid);
             } else {
-                value_meta(cur);
+                value_meta(cur, std::false_type{});
                 values_int2(cur + 4);
             }
         } else {
