@@ -980,9 +980,11 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
 // Merge the piece partials (and the fp16 tail) of one (sequence, KV head)
 // into the outputs of its HB query heads.  The pieces of (b, h) are those of
 // the workgroups owning its first and its last unit and every workgroup in
-// between, at records (b*Hkv + h) + w.  512 threads: thread (tgi, qd) owns
+// between, at records (b*Hkv + h) + w.  512 threads: thread (qd, tgi) owns
 // channel quad qd and merges pieces tgi, tgi + TGR, ... online, with its
-// loads batched so that they are in flight together.
+// loads batched so that they are in flight together; the TGR threads of one
+// quad are adjacent lanes, so their states then meet in a butterfly of lane
+// exchanges, with no LDS round and no barrier.
 //
 // Finding the pieces takes a load of the segment counts and the split
 // arithmetic, and the records can only be loaded after that.  When the
@@ -995,15 +997,14 @@ template <int D, int HB>
 __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
     constexpr int NT = 512;
     constexpr int QPR = D / 4;            // float4 quads per record
-    constexpr int TGR = NT / QPR;         // piece groups
+    constexpr int TGR = NT / QPR;         // piece groups (adjacent lanes of one quad)
+    static_assert(TGR == 16 || TGR == 32, "butterfly width");
     constexpr int BATCH = 2;
     __shared__ float ts[4096];            // tail scores (log2 domain)
-    __shared__ float4 red_o[NT];
-    __shared__ float2 red_ml[NT];
     __shared__ int s_range[2];
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv, h = bh % p.Hkv;
-    const int tid = threadIdx.x, qd = tid % QPR, tgi = tid / QPR;
+    const int tid = threadIdx.x, tgi = tid % TGR, qd = tid / TGR;
     const int nslots = p.B * p.Hkv + p.G;   // records in the workspace (per query head of the group)
     const int wg = max(0, (int)(((long long)bh * p.G) / (p.B * p.Hkv)) - 1);
     float2 sml[HB];
@@ -1046,6 +1047,7 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
     for (int hb = 0; hb < HB; ++hb) {
         const int hq = h * HB + hb;
         if (p.tail_len > 0) {
+            if (hb > 0) __syncthreads();          // the previous head's tail scores are read
             const uint16_t* qp = p.q + ((size_t)b * p.Hq + hq) * D;
             const uint16_t* tk = p.tail_k + (size_t)bh * p.tail_stride * D;
             for (int t = tid; t < p.tail_len; t += NT) {
@@ -1093,23 +1095,19 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
                 merge_run<4>(m, l, o, ts[t], 1.f, vf);
             }
         }
-        red_o[tid] = make_float4(o[0], o[1], o[2], o[3]);
-        red_ml[tid] = make_float2(m, l);
-        __syncthreads();
-        if (tid < QPR) {
-            float mm = -INFINITY, ll = 0.f;
-            float oo[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int gi = 0; gi < TGR; ++gi) {
-                const float4 x = red_o[gi * QPR + tid];
-                const float2 y = red_ml[gi * QPR + tid];
-                const float o2[4] = {x.x, x.y, x.z, x.w};
-                merge_run<4>(mm, ll, oo, y.x, y.y, o2);
-            }
-            const float inv = ll > 0.f ? 1.f / ll : 0.f;
-            *reinterpret_cast<float4*>(p.out + ((size_t)b * p.Hq + hq) * D + 4 * tid) =
-                make_float4(oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv);
+        // the TGR states of this quad: butterfly over adjacent lanes
+#pragma unroll
+        for (int off = 1; off < TGR; off <<= 1) {
+            const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+            const float o2[4] = {__shfl_xor(o[0], off), __shfl_xor(o[1], off), __shfl_xor(o[2], off),
+                                 __shfl_xor(o[3], off)};
+            merge_run<4>(m, l, o, m2, l2, o2);
         }
-        __syncthreads();
+        if (tgi == 0) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            *reinterpret_cast<float4*>(p.out + ((size_t)b * p.Hq + hq) * D + 4 * qd) =
+                make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+        }
     }
 }
 
