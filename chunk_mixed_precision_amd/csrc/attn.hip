@@ -980,43 +980,41 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
 // Merge the piece partials (and the fp16 tail) of one (sequence, KV head)
 // into the outputs of its HB query heads.  The pieces of (b, h) are those of
 // the workgroups owning its first and its last unit and every workgroup in
-// between, at records (b*Hkv + h) + w.  512 threads: thread (qd, tgi) owns
-// channel quad qd and merges pieces tgi, tgi + TGR, ... online, with its
-// loads batched so that they are in flight together; the TGR threads of one
-// quad are adjacent lanes, so their states then meet in a butterfly of lane
-// exchanges, with no LDS round and no barrier.
+// between, at records (b*Hkv + h) + w.  512 threads: thread (hb, qd, tgi)
+// owns channel quad qd of query head hb and merges pieces tgi, tgi + TG, ...
+// online, with its loads batched so that they are in flight together; the TG
+// threads of one (head, quad) are adjacent lanes, so their states then meet
+// in a butterfly of lane exchanges.  All heads are merged at once.
 //
 // Finding the pieces takes a load of the segment counts and the split
 // arithmetic, and the records can only be loaded after that.  When the
 // streams have equal cost (one sequence, or sequences of equal mix) the first
 // owner of stream bh is floor(bh*G/(B*Hkv)) up to rounding, so every thread
-// first loads its share of the TGR records from one below that guess on;
+// first loads its share of the TG records from one below that guess on;
 // when the true pieces lie inside that window (the common case) the merge
 // uses them and waits for one round of loads instead of two.
 template <int D, int HB>
 __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
     constexpr int NT = 512;
     constexpr int QPR = D / 4;            // float4 quads per record
-    constexpr int TGR = NT / QPR;         // piece groups (adjacent lanes of one quad)
-    static_assert(TGR == 16 || TGR == 32, "butterfly width");
+    constexpr int TG = NT / (QPR * HB);   // piece groups per (head, quad): adjacent lanes
+    static_assert(TG >= 4 && TG <= 32 && (TG & (TG - 1)) == 0, "butterfly width");
     constexpr int BATCH = 2;
-    __shared__ float ts[4096];            // tail scores (log2 domain)
+    __shared__ float ts[HB][4096];        // tail scores (log2 domain)
     __shared__ int s_range[2];
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv, h = bh % p.Hkv;
-    const int tid = threadIdx.x, tgi = tid % TGR, qd = tid / TGR;
+    const int tid = threadIdx.x, tgi = tid % TG, qd = (tid / TG) % QPR, hb = tid / (TG * QPR);
+    const int hq = h * HB + hb;
     const int nslots = p.B * p.Hkv + p.G;   // records in the workspace (per query head of the group)
     const int wg = max(0, (int)(((long long)bh * p.G) / (p.B * p.Hkv)) - 1);
-    float2 sml[HB];
-    float4 sov[HB];
+    float2 sml;
+    float4 sov;
     {
         const int slot = min(bh + wg + tgi, nslots - 1);
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            const float* rec = p.part + ((size_t)slot * HB + hb) * (D + 4);
-            sml[hb] = *reinterpret_cast<const float2*>(rec + D);
-            sov[hb] = *reinterpret_cast<const float4*>(rec + 4 * qd);
-        }
+        const float* rec = p.part + ((size_t)slot * HB + hb) * (D + 4);
+        sml = *reinterpret_cast<const float2*>(rec + D);
+        sov = *reinterpret_cast<const float4*>(rec + 4 * qd);
     }
     if (tid < 64) {
         int w0 = 0, np = 0;
@@ -1037,77 +1035,70 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
             s_range[1] = np;
         }
     }
+    if (p.tail_len > 0) {
+        // scores of the tail tokens for every head of the group
+        const uint16_t* tk = p.tail_k + (size_t)bh * p.tail_stride * D;
+        for (int i = tid; i < HB * p.tail_len; i += NT) {
+            const int th = i / p.tail_len, t = i % p.tail_len;
+            const uint16_t* qp = p.q + ((size_t)b * p.Hq + h * HB + th) * D;
+            float s = 0.f;
+            for (int c = 0; c < D; ++c)
+                s = __builtin_fmaf((float)__builtin_bit_cast(_Float16, qp[c]),
+                                   (float)__builtin_bit_cast(_Float16, tk[(size_t)t * D + c]), s);
+            ts[th][t] = s * p.qscale;
+        }
+    }
     __syncthreads();
     const int w0 = s_range[0], npiece = s_range[1];
-    const bool spec = w0 >= wg && w0 + npiece <= wg + TGR;   // all pieces inside the loaded window
-    auto rec_of = [&](int v, int hb) {
-        return p.part + ((size_t)(bh + w0 + v) * HB + hb) * (D + 4);
-    };
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        const int hq = h * HB + hb;
-        if (p.tail_len > 0) {
-            if (hb > 0) __syncthreads();          // the previous head's tail scores are read
-            const uint16_t* qp = p.q + ((size_t)b * p.Hq + hq) * D;
-            const uint16_t* tk = p.tail_k + (size_t)bh * p.tail_stride * D;
-            for (int t = tid; t < p.tail_len; t += NT) {
-                float s = 0.f;
-                for (int c = 0; c < D; ++c)
-                    s = __builtin_fmaf((float)__builtin_bit_cast(_Float16, qp[c]),
-                                       (float)__builtin_bit_cast(_Float16, tk[(size_t)t * D + c]), s);
-                ts[t] = s * p.qscale;
-            }
-            __syncthreads();
+    const bool spec = w0 >= wg && w0 + npiece <= wg + TG;    // all pieces inside the loaded window
+    float m = -INFINITY, l = 0.f;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    if (spec) {
+        // piece wg + tgi - w0 (a valid piece's slot is always below nslots)
+        const int v = wg + tgi - w0;
+        if (v >= 0 && v < npiece) {
+            const float o2[4] = {sov.x, sov.y, sov.z, sov.w};
+            merge_run<4>(m, l, o, sml.x, sml.y, o2);
         }
-        float m = -INFINITY, l = 0.f;
-        float o[4] = {0.f, 0.f, 0.f, 0.f};
-        if (spec) {
-            // piece wg + tgi - w0 (a valid piece's slot is always below nslots)
-            const int v = wg + tgi - w0;
-            if (v >= 0 && v < npiece) {
-                const float o2[4] = {sov[hb].x, sov[hb].y, sov[hb].z, sov[hb].w};
-                merge_run<4>(m, l, o, sml[hb].x, sml[hb].y, o2);
-            }
-        } else for (int v0 = tgi; v0 < npiece; v0 += TGR * BATCH) {
-            float2 ml[BATCH];
-            float4 ov[BATCH];
+    } else for (int v0 = tgi; v0 < npiece; v0 += TG * BATCH) {
+        float2 ml[BATCH];
+        float4 ov[BATCH];
 #pragma unroll
-            for (int j = 0; j < BATCH; ++j) {
-                const int v = v0 + j * TGR;
-                const float* rec = rec_of(v < npiece ? v : v0, hb);
-                ml[j] = *reinterpret_cast<const float2*>(rec + D);
-                ov[j] = *reinterpret_cast<const float4*>(rec + 4 * qd);
-                if (v >= npiece) ml[j].x = -INFINITY;
-            }
+        for (int j = 0; j < BATCH; ++j) {
+            const int v = v0 + j * TG;
+            const float* rec = p.part + ((size_t)(bh + w0 + (v < npiece ? v : v0)) * HB + hb) * (D + 4);
+            ml[j] = *reinterpret_cast<const float2*>(rec + D);
+            ov[j] = *reinterpret_cast<const float4*>(rec + 4 * qd);
+            if (v >= npiece) ml[j].x = -INFINITY;
+        }
 #pragma unroll
-            for (int j = 0; j < BATCH; ++j) {
-                if (ml[j].x == -INFINITY) continue;
-                const float o2[4] = {ov[j].x, ov[j].y, ov[j].z, ov[j].w};
-                merge_run<4>(m, l, o, ml[j].x, ml[j].y, o2);
-            }
+        for (int j = 0; j < BATCH; ++j) {
+            if (ml[j].x == -INFINITY) continue;
+            const float o2[4] = {ov[j].x, ov[j].y, ov[j].z, ov[j].w};
+            merge_run<4>(m, l, o, ml[j].x, ml[j].y, o2);
         }
-        if (p.tail_len > 0) {
-            const uint16_t* tv = p.tail_v + (size_t)bh * p.tail_stride * D + 4 * qd;
-            for (int t = tgi; t < p.tail_len; t += TGR) {
-                float vf[4];
+    }
+    if (p.tail_len > 0) {
+        const uint16_t* tv = p.tail_v + (size_t)bh * p.tail_stride * D + 4 * qd;
+        for (int t = tgi; t < p.tail_len; t += TG) {
+            float vf[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) vf[c] = (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + c]);
-                merge_run<4>(m, l, o, ts[t], 1.f, vf);
-            }
+            for (int c = 0; c < 4; ++c) vf[c] = (float)__builtin_bit_cast(_Float16, tv[(size_t)t * D + c]);
+            merge_run<4>(m, l, o, ts[hb][t], 1.f, vf);
         }
-        // the TGR states of this quad: butterfly over adjacent lanes
+    }
+    // the TG states of this (head, quad): butterfly over adjacent lanes
 #pragma unroll
-        for (int off = 1; off < TGR; off <<= 1) {
-            const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
-            const float o2[4] = {__shfl_xor(o[0], off), __shfl_xor(o[1], off), __shfl_xor(o[2], off),
-                                 __shfl_xor(o[3], off)};
-            merge_run<4>(m, l, o, m2, l2, o2);
-        }
-        if (tgi == 0) {
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            *reinterpret_cast<float4*>(p.out + ((size_t)b * p.Hq + hq) * D + 4 * qd) =
-                make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-        }
+    for (int off = 1; off < TG; off <<= 1) {
+        const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+        const float o2[4] = {__shfl_xor(o[0], off), __shfl_xor(o[1], off), __shfl_xor(o[2], off),
+                             __shfl_xor(o[3], off)};
+        merge_run<4>(m, l, o, m2, l2, o2);
+    }
+    if (tgi == 0) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        *reinterpret_cast<float4*>(p.out + ((size_t)b * p.Hq + hq) * D + 4 * qd) =
+            make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
     }
 }
 
