@@ -20,10 +20,11 @@
 // second launch merges the partials of each (sequence, head).
 //
 // A wavefront is split into R = 64/S rows of S = d/8 lanes; each row handles
-// one group block per iteration for one query head, or for two with
-// grouped-query attention (with four heads per KV head, two rows share a
-// group block).  Inside a row, lane slot L owns channels 8L..8L+7 of the keys
-// and value group L % (d/32) of tokens L / (d/32) + 4m.
+// one group block per iteration for one query head, or for two with two query
+// heads per KV head.  With four heads per KV head two rows share a group block
+// and split its data (keys by token, values by channel), each serving all
+// four heads (run_piece_g4).  Inside a row, lane slot L owns channels
+// 8L..8L+7 of the keys and value group L % (d/32) of tokens L / (d/32) + 4m.
 //
 // Scores: s_t = sum_j q_j * (code_tj * s_j + mn_j) is evaluated as
 // sum_j (q_j s_j) code_tj + sum_j q_j mn_j, so key dequantization costs one
@@ -905,6 +906,590 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     __syncthreads();
 }
 
+
+// ---------------------------------------------------------------- four query heads per KV head
+// With four query heads per KV head the two rows of a row pair share one
+// group block and split its data, not its heads: row hs takes the key tokens
+// of position bit 3 equal to hs in each half (through the token xor: the
+// lane's key words of position block hs ^ top) and the value channels
+// 16hs .. 16hs+15 of each group, and both rows serve all four heads.  Every
+// code is unpacked once, for four FMAs, and every lane loads only the rows
+// (or the half cells) it uses: an FP16 unit takes 4 load phases, an INT4 or
+// INT2 unit 2.
+//
+// The key state of a lane lists its heads in the order j ^ sg, sg = 2 in the
+// lanes of the upper half of a row (top) and 0 otherwise, so that the first
+// butterfly step of the reduce-scatter, which pairs lanes of opposite top,
+// hands each lane two of the four heads without a select.  Value state (o,
+// pm, the value weights) is in natural head order.
+template <int D>
+__device__ __forceinline__ void run_piece_g4(const AttnParams& p, const SeqUnits<D, 4>& su, int b, int h, int U0,
+                                             int U1, int tbase, int slot, int* ctr, float* plds, float* rec) {
+    constexpr int HB = 4;
+    constexpr int S = D / 8;
+    constexpr int R = 64 / S;          // rows per wave
+    constexpr int NG = D / 32;         // value groups per token
+    constexpr int GPI = R / 2;         // group blocks per unit: one per row pair
+    constexpr int NTH = 16 / S;        // tokens per lane, head and key half after the reduce-scatter
+    constexpr int RECF = D + 4;
+    constexpr uint32_t ROWB = (uint32_t)S * 16u;
+    constexpr int FIRST = S == 16 ? kDppRowMirror : kDppRowHalfMirror;   // partner of opposite top
+    static_assert(GPI == SeqUnits<D, HB>::GPI, "unit geometry");
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = lane / S, L = lane % S;
+    const int hs = row & 1, gslot = row >> 1;
+    const int G = L % NG, tq = L / NG;
+    const int fx = tok_xor(S, L);
+    const bool top = L >= S / 2;
+    const int sg = top ? 2 : 0;
+    const int ws = hs ^ (top ? 1 : 0);   // the lane's key position block (bit 3 of the position)
+    const int bh = b * p.Hkv + h;
+
+    const size_t gpc = (size_t)(p.C / kGroup);
+    const uint8_t* seg16 = p.pool[0] + (size_t)bh * p.cap[0] * gpc * group_bytes(16, D);
+    const uint8_t* seg4 = p.pool[1] + (size_t)bh * p.cap[1] * gpc * group_bytes(4, D);
+    const uint8_t* seg2 = p.pool[2] + (size_t)bh * p.cap[2] * gpc * group_bytes(2, D);
+
+    // per-lane byte offsets inside a group block
+    const uint32_t k16 = (uint32_t)(8 * ws) * ROWB;                 // FP16 key rows 16hh + 8ws + i
+    const uint32_t v16 = (uint32_t)(32 + 2 * hs) * ROWB;            // FP16 value rows 32 + 4m + 2hs + k
+    const uint32_t k4 = (uint32_t)(4 + 2 * ws) * ROWB;              // INT4 key code rows 4 + 4hh + 2ws + i
+    const uint32_t v4 = 16u * ROWB + 8u * (uint32_t)hs;             // INT4 value code rows 16 + m, bytes 8hs..
+    const uint32_t psel = ws ? 0x07060302u : 0x05040100u;          // INT2 keys: the 16-bit half of block ws
+
+    uint4 bufA[8], bufB[8];
+    auto grab = [&]() -> int {
+        int t = 0;
+        if (lane == 0) t = atomicAdd(ctr, 1);
+        return U0 + (__builtin_amdgcn_readfirstlane(t) - tbase);
+    };
+    auto unit_addr = [&](int U, uint32_t& voff) -> const uint8_t* {
+        int k = 0, u = U;
+        const uint8_t* base = seg16;
+        uint32_t gb = (uint32_t)group_bytes(16, D);
+        if (U >= su.ubase[2]) {
+            k = 2; u = U - su.ubase[2]; base = seg2; gb = (uint32_t)group_bytes(2, D);
+        } else if (U >= su.ubase[1]) {
+            k = 1; u = U - su.ubase[1]; base = seg4; gb = (uint32_t)group_bytes(4, D);
+        }
+        const int segg = k == 0 ? su.segg[0] : (k == 1 ? su.segg[1] : su.segg[2]);
+        const bool live = u * GPI + gslot < segg;
+        voff = (live ? (uint32_t)gslot * gb : 0u) + (uint32_t)L * 16u;
+        return base + (size_t)u * GPI * gb;
+    };
+    typedef unsigned u32x2_nt __attribute__((ext_vector_type(2)));
+    auto ld8 = [](const uint8_t* a) -> uint2 {
+        const u32x2_nt x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(a));
+        return make_uint2(x.x, x.y);
+    };
+    // the rows of load phase ph of a unit of BITS-bit codes
+    auto load_phase = [&](auto bits_tag, uint4* buf, const uint8_t* base, uint32_t voff, int ph) {
+        constexpr int BITS = decltype(bits_tag)::value;
+        const uint8_t* a = base + voff;
+        if constexpr (BITS == 16) {
+            if (ph < 2) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) buf[i] = ld16(a + k16 + (uint32_t)(16 * ph + i) * ROWB);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    buf[i] = ld16(a + v16 + (uint32_t)(16 * (ph - 2) + 4 * (i >> 1) + (i & 1)) * ROWB);
+            }
+        } else if constexpr (BITS == 4) {
+            if (ph == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) buf[i] = ld16(a + (uint32_t)i * ROWB);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) buf[4 + i] = ld16(a + k4 + (uint32_t)(4 * (i >> 1) + (i & 1)) * ROWB);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) buf[i] = ld16(a + (uint32_t)(12 + i) * ROWB);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint2 x = ld8(a + v4 + (uint32_t)(2 * i) * ROWB);
+                    const uint2 y = ld8(a + v4 + (uint32_t)(2 * i + 1) * ROWB);
+                    buf[4 + i] = make_uint4(x.x, x.y, y.x, y.y);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) buf[i] = ld16(a + (uint32_t)(8 * ph + i) * ROWB);
+        }
+    };
+
+    // Phase 0 of a unit of any segment k (wave-uniform) without a branch:
+    // the rows are uniform (FP16 0-7, INT4 0-5 and 8-9, INT2 0-7) and the
+    // lane's position-block offset applies to the FP16 rows and the INT4 code
+    // rows.
+    auto load_first = [&](uint4* buf, const uint8_t* base, uint32_t voff, int k) {
+        const uint32_t va = voff + (k == 0 ? k16 : 0u);
+        const uint32_t vb = voff + (k == 0 ? k16 : (k == 1 ? k4 - 4u * ROWB : 0u));
+        const uint32_t r6 = (k == 1 ? 8u : 6u) * ROWB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf[i] = ld16(base + va + (uint32_t)i * ROWB);
+        buf[4] = ld16(base + vb + 4u * ROWB);
+        buf[5] = ld16(base + vb + 5u * ROWB);
+        buf[6] = ld16(base + r6 + vb);
+        buf[7] = ld16(base + r6 + vb + ROWB);
+    };
+    auto seg_of = [&](int U_) { return U_ >= su.ubase[2] ? 2 : (U_ >= su.ubase[1] ? 1 : 0); };
+
+    int U = grab();
+    uint32_t vo = 0;
+    const uint8_t* ub = seg16;
+    if (U < U1) {
+        ub = unit_addr(U, vo);
+        load_first(bufA, ub, vo, seg_of(U));
+    }
+
+    // query channels 8L..8L+7 of the four heads, in key-state order
+    uint32_t qw[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 qc = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + h * HB + (j ^ sg)) * D + 8 * L);
+        qw[j][0] = qc.x; qw[j][1] = qc.y; qw[j][2] = qc.z; qw[j][3] = qc.w;
+    }
+    float qs[4][8];        // q * log2(e)/sqrt(d) in fp32 (INT-b keys), key-state order
+
+    float M[2];            // running max of heads j ^ sg (j = 0, 1): uniform over the row pair's holders
+    float lsum[2];         // this lane's share of their softmax denominators
+    float o[4][16];        // value channels 32G + 16hs + c, natural head order
+    float pm[4];           // sum_t p_t * mn_t over this lane's value tokens
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        M[j] = -INFINITY;
+        lsum[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        pm[j] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) o[j][c] = 0.f;
+    }
+    float sc[2][2 * NTH];  // key scores of heads j ^ sg: half 0, then half 1
+    float pw[4][8];        // value weights of tokens tq + 4m: p (FP16), p * scale (INT-b)
+    float koff[4];         // initial key accumulators: sum_j q_j mn_j
+    float acc[4][8];       // key partial sums of the lane's 8 positions of one half
+
+    // Reduce-scatter of one half over the S lanes of a row: the first step
+    // pairs lanes of opposite top (same tokens, heads swapped), the others
+    // halve the positions as the token xor dictates.
+    auto take_half = [&](int hh) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int g = 0; g < 8; ++g) acc[j][g] += dpp<FIRST>(acc[j + 2][g]);
+        if constexpr (S == 16) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) acc[j][g] += dpp<kDppRowHalfMirror>(acc[j][g + 4]);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) acc[j][g] += dpp<kDppXor2>(acc[j][g + 2]);
+                acc[j][0] += dpp<kDppXor1>(acc[j][1]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) acc[j][g] += dpp<kDppXor2>(acc[j][g + 4]);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) acc[j][g] += dpp<kDppXor1>(acc[j][g + 2]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int g = 0; g < NTH; ++g) sc[j][hh * NTH + g] = acc[j][g];
+    };
+    // max over the lanes of the row pair that hold the same heads
+    auto pair_max = [&](float v) {
+        v = fmaxf(v, dpp<kDppXor1>(v));
+        v = fmaxf(v, dpp<kDppXor2>(v));
+        if constexpr (S == 16) {
+            v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+            v = fmaxf(v, __shfl_xor(v, 16));
+        } else {
+            v = fmaxf(v, dpp<0x128>(v));   // row_ror:8, the other row of the pair
+        }
+        return v;
+    };
+    // the values of heads 0..3 (natural order) from x[j] of heads j ^ sg,
+    // j = 0, 1, here and at the first-step partner (heads j ^ sg ^ 2)
+    auto natural4 = [&](const float* x, float* nat) {
+        const float y0 = dpp<FIRST>(x[0]), y1 = dpp<FIRST>(x[1]);
+        nat[0] = top ? y0 : x[0];
+        nat[1] = top ? y1 : x[1];
+        nat[2] = top ? x[0] : y0;
+        nat[3] = top ? x[1] : y1;
+    };
+
+    auto softmax_step = [&](bool valid) {
+        float al[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 2 * NTH; ++i) {
+                if (!valid) sc[j][i] = -INFINITY;
+                mloc = fmaxf(mloc, sc[j][i]);
+            }
+            mloc = pair_max(mloc);
+            const float Mn = fmaxf(M[j], mloc);
+            al[j] = (Mn == -INFINITY) ? 1.f : fast_exp2(M[j] - Mn);
+            M[j] = Mn;
+            float pt[2 * NTH];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 2 * NTH; ++i) {
+                pt[i] = valid ? fast_exp2(sc[j][i] - Mn) : 0.f;
+                psum += pt[i];
+            }
+            lsum[j] = __builtin_fmaf(lsum[j], al[j], psum);
+            // slot of token t in the value layout: (t & 3) * 8 + (t >> 2)
+            float* pl = plds + (gslot * HB + (j ^ sg)) * 32;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int g = 0; g < NTH; ++g) {
+                    const int t = 16 * hh + 8 * hs + ((g ^ fx) & 7);
+                    pl[(t & 3) * 8 + (t >> 2)] = pt[hh * NTH + g];
+                }
+        }
+        // the value state is rescaled only when some head's maximum rose
+        // (the factor is exactly 1 otherwise)
+        if (__ballot(al[0] != 1.f || al[1] != 1.f)) {
+            float an[4];
+            natural4(al, an);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pm[j] *= an[j];
+#pragma unroll
+                for (int c = 0; c < 16; ++c) o[j][c] *= an[j];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float* pl = plds + (gslot * HB + j) * 32;
+            const float4 pa = *reinterpret_cast<const float4*>(pl + tq * 8);
+            const float4 pb = *reinterpret_cast<const float4*>(pl + tq * 8 + 4);
+            pw[j][0] = pa.x; pw[j][1] = pa.y; pw[j][2] = pa.z; pw[j][3] = pa.w;
+            pw[j][4] = pb.x; pw[j][5] = pb.y; pw[j][6] = pb.z; pw[j][7] = pb.w;
+        }
+    };
+
+    // ---- INT-b pieces (codes converted to fp32 by v_cvt_f32_ubyte, once for the four heads)
+    // The key weight of channel e and head j is q_j * s_e, formed where it
+    // is used from the scale rows that stay in the phase buffer (a second
+    // time for the second half), which keeps 32 weights out of the registers.
+    auto key_meta = [&](const uint4* m4) {   // rows: scale lo, scale hi, min lo, min hi
+        const float4 n0 = as_f4(m4[2]), n1 = as_f4(m4[3]);
+        const float kmn[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float bias = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bias = __builtin_fmaf(qs[j][e], kmn[e], bias);
+            koff[j] = bias;
+        }
+    };
+    auto key_scale = [](const uint4* m4, int ch) {
+        const uint4 r = m4[ch >> 2];
+        const uint32_t x = (ch & 3) == 0 ? r.x : (ch & 3) == 1 ? r.y : (ch & 3) == 2 ? r.z : r.w;
+        return __builtin_bit_cast(float, x);
+    };
+    // the lane's 2 INT4 key rows of one half: word e of row ii holds channel
+    // 4ii + e at its 8 positions g (nibble g)
+    auto key_half_int4 = [&](const uint4* m4, const uint4* rows) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 8; ++g) acc[j][g] = koff[j];
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const uint32_t wd[4] = {rows[ii].x, rows[ii].y, rows[ii].z, rows[ii].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = wd[e] & 0x0F0F0F0Fu, hi = (wd[e] >> 4) & 0x0F0F0F0Fu;
+                const float c[8] = {cvt_ub<0>(lo), cvt_ub<0>(hi), cvt_ub<1>(lo), cvt_ub<1>(hi),
+                                    cvt_ub<2>(lo), cvt_ub<2>(hi), cvt_ub<3>(lo), cvt_ub<3>(hi)};
+                const float ks = key_scale(m4, 4 * ii + e);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float wq = qs[j][4 * ii + e] * ks;
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) acc[j][g] = __builtin_fmaf(wq, c[g], acc[j][g]);
+                }
+            }
+        }
+    };
+    // the 2 INT2 key rows of one half: word e of row ii holds channel 4ii + e
+    // at positions 0..15 (bits 2f); the lane takes positions 8ws .. 8ws+7,
+    // the 16-bit half ws of the word, pairing two words in one register
+    auto key_half_int2 = [&](const uint4* m4, const uint4* rows) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 8; ++g) acc[j][g] = koff[j];
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const uint32_t wd[4] = {rows[ii].x, rows[ii].y, rows[ii].z, rows[ii].w};
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                // bytes: [word 2e2, half ws] [word 2e2+1, half ws]
+                const uint32_t y = __builtin_amdgcn_perm(wd[2 * e2 + 1], wd[2 * e2], psel);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    // byte 0: position k, byte 1: k + 4 of word 2e2; bytes 2, 3 the same of word 2e2+1
+                    const uint32_t z = (y >> (2 * k)) & 0x03030303u;
+                    const float c0 = cvt_ub<0>(z), c1 = cvt_ub<1>(z), c2 = cvt_ub<2>(z), c3 = cvt_ub<3>(z);
+                    const float sa = key_scale(m4, 4 * ii + 2 * e2), sb = key_scale(m4, 4 * ii + 2 * e2 + 1);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float wa = qs[j][4 * ii + 2 * e2] * sa, wb = qs[j][4 * ii + 2 * e2 + 1] * sb;
+                        acc[j][k] = __builtin_fmaf(wa, c0, acc[j][k]);
+                        acc[j][k + 4] = __builtin_fmaf(wa, c1, acc[j][k + 4]);
+                        acc[j][k] = __builtin_fmaf(wb, c2, acc[j][k]);
+                        acc[j][k + 4] = __builtin_fmaf(wb, c3, acc[j][k + 4]);
+                    }
+                }
+            }
+        }
+    };
+    auto value_meta = [&](const uint4* m4) {   // (scale, min) of tokens t_{2r}, t_{2r+1}
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float4 sm = as_f4(m4[m >> 1]);
+            const float s = (m & 1) ? sm.z : sm.x;
+            const float mn = (m & 1) ? sm.w : sm.y;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pm[j] = __builtin_fmaf(pw[j][m], mn, pm[j]);
+                pw[j][m] *= s;
+            }
+        }
+    };
+    // token tq + 4m: dwords 2m, 2m + 1 of the buffer (channels 16hs + 8uu + f)
+    auto values_int4 = [&](const uint4* rows) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint4 cw = rows[m >> 1];
+            const uint32_t wd[2] = {(m & 1) ? cw.z : cw.x, (m & 1) ? cw.w : cw.y};
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+                const uint32_t lo = wd[uu] & 0x0F0F0F0Fu, hi = (wd[uu] >> 4) & 0x0F0F0F0Fu;
+                const float c[8] = {cvt_ub<0>(lo), cvt_ub<0>(hi), cvt_ub<1>(lo), cvt_ub<1>(hi),
+                                    cvt_ub<2>(lo), cvt_ub<2>(hi), cvt_ub<3>(lo), cvt_ub<3>(hi)};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float wv = pw[j][m];
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) o[j][8 * uu + g] = __builtin_fmaf(wv, c[g], o[j][8 * uu + g]);
+                }
+            }
+        }
+    };
+    // row r: tokens t_{2r} (dwords 0, 1), t_{2r+1} (dwords 2, 3); dword u of a
+    // token holds channels 16u .. 16u+15 of the group, the lane takes u = hs
+    auto values_int2 = [&](const uint4* rows) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint4 cw = rows[m >> 1];
+            const uint32_t x = (m & 1) ? (hs ? cw.w : cw.z) : (hs ? cw.y : cw.x);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // byte q: channel 4q + k
+                const uint32_t z = (x >> (2 * k)) & 0x03030303u;
+                const float c[4] = {cvt_ub<0>(z), cvt_ub<1>(z), cvt_ub<2>(z), cvt_ub<3>(z)};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float wv = pw[j][m];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) o[j][4 * q4 + k] = __builtin_fmaf(wv, c[q4], o[j][4 * q4 + k]);
+                }
+            }
+        }
+    };
+
+    // ---- FP16 pieces: the lane's 8 key rows of one half (q . k with v_dot2),
+    // or its 8 value rows of tokens tq + 4m, m = 4mb .. 4mb + 3
+    auto keys_fp16 = [&](const uint4* rows) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float a = __builtin_amdgcn_fdot2(as_h2(rows[i].x), as_h2(qw[j][0]), 0.f, false);
+                a = __builtin_amdgcn_fdot2(as_h2(rows[i].y), as_h2(qw[j][1]), a, false);
+                a = __builtin_amdgcn_fdot2(as_h2(rows[i].z), as_h2(qw[j][2]), a, false);
+                a = __builtin_amdgcn_fdot2(as_h2(rows[i].w), as_h2(qw[j][3]), a, false);
+                acc[j][i] = a;
+            }
+    };
+    auto values_fp16 = [&](const uint4* rows, int mb) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int m = 4 * mb + (i >> 1), cb = 8 * (i & 1);
+            const uint32_t wd[4] = {rows[i].x, rows[i].y, rows[i].z, rows[i].w};
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = lo_h(wd[e]);
+                f[2 * e + 1] = hi_h(wd[e]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float pr = pw[j][m];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) o[j][cb + c] = __builtin_fmaf(pr, f[c], o[j][cb + c]);
+            }
+        }
+    };
+
+    auto compute_phase = [&](auto bits_tag, int ph, const uint4* cur, bool valid) {
+        constexpr int BITS = decltype(bits_tag)::value;
+        if constexpr (BITS == 16) {
+            if (ph < 2) {
+                keys_fp16(cur);
+                take_half(ph);
+                if (ph == 1) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int i = 0; i < 2 * NTH; ++i) sc[j][i] *= p.qscale;
+                    softmax_step(valid);
+                }
+            } else {
+                values_fp16(cur, ph - 2);
+            }
+        } else {
+            if (ph == 0) {
+                key_meta(cur);
+                if constexpr (BITS == 4) key_half_int4(cur, cur + 4);
+                else key_half_int2(cur, cur + 4);
+                take_half(0);
+                if constexpr (BITS == 4) key_half_int4(cur, cur + 6);
+                else key_half_int2(cur, cur + 6);
+                take_half(1);
+                softmax_step(valid);
+            } else {
+                value_meta(cur);
+                if constexpr (BITS == 4) values_int4(cur + 4);
+                else values_int2(cur + 4);
+            }
+        }
+    };
+
+    // ---- unit loop: as in the general path, loads one phase ahead in the
+    // other buffer; every segment has an even phase count here
+    auto run_unit = [&](auto bits_tag, const uint8_t* ub_, uint32_t vo_, int kn, const uint8_t* ubn, uint32_t von,
+                        bool valid) {
+        constexpr int BITS = decltype(bits_tag)::value;
+        constexpr int NPH = BITS == 16 ? 4 : 2;
+#pragma unroll
+        for (int ph = 0; ph < NPH; ++ph) {
+            uint4* cur = (ph & 1) ? bufB : bufA;
+            uint4* nxt = (ph & 1) ? bufA : bufB;
+            if (ph + 1 < NPH) load_phase(bits_tag, nxt, ub_, vo_, ph + 1);
+            else load_first(nxt, ubn, von, kn);   // the next unit, or a stand-in re-read of this one
+            __builtin_amdgcn_sched_barrier(0);
+            compute_phase(bits_tag, ph, cur, valid);
+        }
+    };
+    auto step = [&](auto bits_tag, int segg_k, int ubase_k) {
+        constexpr int BITS = decltype(bits_tag)::value;
+        const int Un = grab();
+        uint32_t von = 0;   // no next unit: every lane re-reads the unit's first cell (one line per load)
+        const uint8_t* ubn = ub;
+        int kn = expert_of_bits(BITS);
+        if (Un < U1) {
+            ubn = unit_addr(Un, von);
+            kn = seg_of(Un);
+        }
+        const bool valid = (U - ubase_k) * GPI + gslot < segg_k;
+        run_unit(bits_tag, ub, vo, kn, ubn, von, valid);
+        U = Un;
+        ub = ubn;
+        vo = von;
+    };
+    {
+        const int end = min(U1, su.ubase[0] + su.nu[0]);
+        while (U < end) step(std::integral_constant<int, 16>{}, su.segg[0], su.ubase[0]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qs[j][2 * e] = lo_h(qw[j][e]) * p.qscale;
+            qs[j][2 * e + 1] = hi_h(qw[j][e]) * p.qscale;
+        }
+    {
+        const int end = min(U1, su.ubase[1] + su.nu[1]);
+        while (U < end) step(std::integral_constant<int, 4>{}, su.segg[1], su.ubase[1]);
+    }
+    {
+        const int end = min(U1, su.ubase[2] + su.nu[2]);
+        while (U < end) step(std::integral_constant<int, 2>{}, su.segg[2], su.ubase[2]);
+    }
+
+    // ---------------- merge the lanes and row pairs of each head
+    float Mn4[4], ln4[4];
+    natural4(M, Mn4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ln4[j] = ((j >> 1) == (top ? 1 : 0)) ? lsum[j & 1] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float Mx = Mn4[j];
+#pragma unroll
+        for (int off = 2 * S; off < 64; off <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, off));
+
+        const float rs = (Mn4[j] == -INFINITY) ? 0.f : fast_exp2(Mn4[j] - Mx);
+        float l = ln4[j] * rs;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) l += __shfl_xor(l, off);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            float v = (o[j][c] + pm[j]) * rs;
+#pragma unroll
+            for (int off = NG; off < S; off <<= 1) v += __shfl_xor(v, off);
+#pragma unroll
+            for (int off = 2 * S; off < 64; off <<= 1) v += __shfl_xor(v, off);
+            o[j][c] = v;
+        }
+        if (gslot == 0 && tq == 0) {
+            float* r = rec + ((size_t)wave * HB + j) * RECF;
+            float4* o4 = reinterpret_cast<float4*>(r + 32 * G + 16 * hs);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                o4[c] = make_float4(o[j][4 * c], o[j][4 * c + 1], o[j][4 * c + 2], o[j][4 * c + 3]);
+            if (G == 0 && hs == 0) {
+                r[D] = Mx;
+                r[D + 1] = l;
+            }
+        }
+    }
+    __syncthreads();
+    constexpr int QPR = D / 4;
+    if ((int)threadIdx.x < HB * QPR) {
+        const int mh = threadIdx.x / QPR, qd = threadIdx.x % QPR;
+        float m = -INFINITY, l = 0.f, oo[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int wv = 0; wv < kAttnWaves; ++wv) {
+            const float* r = rec + ((size_t)wv * HB + mh) * RECF;
+            const float4 x = *reinterpret_cast<const float4*>(r + 4 * qd);
+            const float o2[4] = {x.x, x.y, x.z, x.w};
+            merge_run<4>(m, l, oo, r[D], r[D + 1], o2);
+        }
+        float* dst = p.part + ((size_t)slot * HB + mh) * RECF;
+        *reinterpret_cast<float4*>(dst + 4 * qd) = make_float4(oo[0], oo[1], oo[2], oo[3]);
+        if (qd == 0) *reinterpret_cast<float4*>(dst + D) = make_float4(m, l, 0.f, 0.f);
+    }
+    __syncthreads();
+}
+
 }  // namespace
 
 // Persistent workgroups of kAttnWaves wavefronts.  Workgroup w takes the cost
@@ -965,7 +1550,10 @@ __global__ __launch_bounds__(64 * kAttnWaves, kAttnWaves / 4) void attn_tile_ker
         const int U0 = su.first_at_or_after(lo - off);
         const int U1 = su.first_at_or_after(hi - off);
         if (U0 < U1) {
-            run_piece<D, HB>(p, su, b, h, U0, U1, tbase, b * p.Hkv + h + w, &ctr, plds, rec);
+            if constexpr (HB == 4)
+                run_piece_g4<D>(p, su, b, h, U0, U1, tbase, b * p.Hkv + h + w, &ctr, plds, rec);
+            else
+                run_piece<D, HB>(p, su, b, h, U0, U1, tbase, b * p.Hkv + h + w, &ctr, plds, rec);
             tbase += U1 - U0 + kAttnWaves;
         }
         off += su.cost;

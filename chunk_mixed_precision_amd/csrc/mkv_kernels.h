@@ -100,20 +100,22 @@ constexpr int kAttnGranule = 512;
 // Largest whole-cache cost, in granules, that the split handles.
 constexpr long long kAttnMaxGranules = (1LL << 31) - 1;
 // Cost of a unit per byte, in sixteenths, for segment k (FP16, INT4, INT2)
-// and hb query heads per KV head: the workgroup time per byte on each
-// segment relative to INT4, fitted from per-workgroup timings with four heads
-// per KV head (with two, halfway between one and four).  With one head per
-// KV head the kernel streams at the same rate on every segment; with
+// and hb query heads per KV head: the time per byte of a cache of that
+// segment alone relative to INT4, measured per kernel variant.  With one head
+// per KV head the kernel streams at the same rate on every segment; with
 // grouped-query heads the arithmetic per byte counts (an INT2 byte holds
 // twice the codes of an INT4 byte, an FP16 byte needs no unpacking).
 // Equal-cost ranges finish together.
 constexpr int attn_cost16(int hb, int k) {
     return hb == 1 ? 16
          : hb == 2 ? (k == 0 ? 11 : k == 1 ? 16 : 22)
-                   : (k == 0 ? 7 : k == 1 ? 16 : 29);
+                   : (k == 0 ? 9 : k == 1 ? 16 : 21);
 }
-// Query heads served by one row of lanes: with grouped-query attention a row
-// serves two heads of its KV head, so each code word is unpacked once for both.
+// Rows of lanes per group block and heads per row, as the unit geometry
+// sees them: with two query heads per KV head a row serves both (each code
+// word is unpacked once for both); with four, a row pair shares a group
+// block (split by data, both rows serving all four heads), which gives the
+// same group blocks per wavefront iteration as two heads per row.
 constexpr int attn_heads_per_row(int hb) { return hb == 1 ? 1 : 2; }
 
 struct AttnParams {
