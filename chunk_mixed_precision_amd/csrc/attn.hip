@@ -317,10 +317,9 @@ __device__ __forceinline__ int seq_containing(const AttnParams& p, int x, int& s
 // ends the piece, so the caller knows the next piece's base.  Leaves one
 // partial per query head of the group at record `slot`.
 //
-// A row serves HPR query heads of the KV head (one when HB = 1, two
-// otherwise): every code word is unpacked once and feeds the HPR heads'
-// FMAs.  With HB = 4 the two rows of a row pair take the same group block
-// for heads {0, 1} and {2, 3}.
+// One or two query heads per KV head: a row serves all HB of them, so every
+// code word is unpacked once and feeds the heads' FMAs.  (Four heads per KV
+// head take run_piece_g4.)
 template <int D, int HB>
 __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D, HB>& su, int b, int h, int U0,
                                           int U1, int tbase, int slot, int* ctr, float* plds, float* rec) {
@@ -328,19 +327,19 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     constexpr int R = 64 / S;          // rows per wave
     constexpr int NG = D / 32;         // value groups per token
     constexpr int HPR = attn_heads_per_row(HB);
-    constexpr int RPG = HB / HPR;      // rows per group block
-    constexpr int GPI = R / RPG;       // group blocks per unit
+    constexpr int GPI = R;             // group blocks per unit: one per row
+    static_assert(HPR == HB, "a row serves every head of its KV head");
     constexpr int NTH = 16 / S;        // tokens per lane and key half after the reduce-scatter
     constexpr int RECF = D + 4;        // floats per merged record
     static_assert(GPI == SeqUnits<D, HB>::GPI, "unit geometry");
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = lane / S, L = lane % S;
-    const int hs = row % RPG, gslot = row / RPG;
+    const int gslot = row;
     const int G = L % NG, tq = L / NG;
     const int fx = tok_xor(S, L);
     const int bh = b * p.Hkv + h;
-    const int hq0 = h * HB + hs * HPR;   // this row's first query head
+    const int hq0 = h * HB;              // this row's first query head
 
     // segment base pointers of this (b, h)
     const size_t gpc = (size_t)(p.C / kGroup);
@@ -858,25 +857,25 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
         for (int c = 0; c < 32; ++c) o[j][c] += pm[j];
         float Mx = M[j];
 #pragma unroll
-        for (int off = S * RPG; off < 64; off <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, off));
+        for (int off = S; off < 64; off <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, off));
         const float rs = (M[j] == -INFINITY) ? 0.f : fast_exp2(M[j] - Mx);
         float l = lsum[j] * rs;
 #pragma unroll
         for (int off = 1; off < S; off <<= 1) l += __shfl_xor(l, off);
 #pragma unroll
-        for (int off = S * RPG; off < 64; off <<= 1) l += __shfl_xor(l, off);
+        for (int off = S; off < 64; off <<= 1) l += __shfl_xor(l, off);
 #pragma unroll
         for (int c = 0; c < 32; ++c) {
             float v = o[j][c] * rs;
 #pragma unroll
             for (int off = NG; off < S; off <<= 1) v += __shfl_xor(v, off);
 #pragma unroll
-            for (int off = S * RPG; off < 64; off <<= 1) v += __shfl_xor(v, off);
+            for (int off = S; off < 64; off <<= 1) v += __shfl_xor(v, off);
             o[j][c] = v;
         }
-        // ---------------- the wavefront's record of head hs*HPR + j, for the workgroup merge
-        if (row == hs && tq == 0) {
-            float* r = rec + ((size_t)wave * HB + hs * HPR + j) * RECF;
+        // ---------------- the wavefront's record of head j, for the workgroup merge
+        if (row == 0 && tq == 0) {
+            float* r = rec + ((size_t)wave * HB + j) * RECF;
             float4* o4 = reinterpret_cast<float4*>(r + 32 * G);
 #pragma unroll
             for (int c = 0; c < 8; ++c)
@@ -954,7 +953,7 @@ __device__ __forceinline__ void run_piece_g4(const AttnParams& p, const SeqUnits
     // per-lane byte offsets inside a group block
     const uint32_t k16 = (uint32_t)(8 * ws) * ROWB;                 // FP16 key rows 16hh + 8ws + i
     const uint32_t v16 = (uint32_t)(32 + 2 * hs) * ROWB;            // FP16 value rows 32 + 4m + 2hs + k
-    const uint32_t k4 = (uint32_t)(4 + 2 * ws) * ROWB;              // INT4 key code rows 4 + 4hh + 2ws + i
+    const uint32_t k4 = (uint32_t)(2 * ws) * ROWB;                  // INT4 key code rows 4 + 4hh + 2ws + i
     const uint32_t v4 = 16u * ROWB + 8u * (uint32_t)hs;             // INT4 value code rows 16 + m, bytes 8hs..
     const uint32_t psel = ws ? 0x07060302u : 0x05040100u;          // INT2 keys: the 16-bit half of block ws
 
@@ -983,38 +982,37 @@ __device__ __forceinline__ void run_piece_g4(const AttnParams& p, const SeqUnits
         const u32x2_nt x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(a));
         return make_uint2(x.x, x.y);
     };
-    // the rows of load phase ph of a unit of BITS-bit codes
+    // The rows of load phase ph >= 1 of a unit of BITS-bit codes (phase 0,
+    // whose unit may be of any segment, is load_first below).
+    //   FP16: 1 = the lane's 8 key rows of half 1, 2 and 3 = its value rows of
+    //         tokens tq + 4m, m = 0..3 and 4..7 (two channel octets each);
+    //   INT4: 1 = value meta rows, then the lane's half cell of the 8 value
+    //         code rows;
+    //   INT2: 1 = value meta and value code rows.
     auto load_phase = [&](auto bits_tag, uint4* buf, const uint8_t* base, uint32_t voff, int ph) {
         constexpr int BITS = decltype(bits_tag)::value;
         const uint8_t* a = base + voff;
         if constexpr (BITS == 16) {
-            if (ph < 2) {
+            if (ph == 1) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) buf[i] = ld16(a + k16 + (uint32_t)(16 * ph + i) * ROWB);
+                for (int i = 0; i < 8; ++i) buf[i] = ld16(a + k16 + (uint32_t)(16 + i) * ROWB);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     buf[i] = ld16(a + v16 + (uint32_t)(16 * (ph - 2) + 4 * (i >> 1) + (i & 1)) * ROWB);
             }
         } else if constexpr (BITS == 4) {
-            if (ph == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) buf[i] = ld16(a + (uint32_t)i * ROWB);
+            for (int i = 0; i < 4; ++i) buf[i] = ld16(a + (uint32_t)(12 + i) * ROWB);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) buf[4 + i] = ld16(a + k4 + (uint32_t)(4 * (i >> 1) + (i & 1)) * ROWB);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) buf[i] = ld16(a + (uint32_t)(12 + i) * ROWB);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint2 x = ld8(a + v4 + (uint32_t)(2 * i) * ROWB);
-                    const uint2 y = ld8(a + v4 + (uint32_t)(2 * i + 1) * ROWB);
-                    buf[4 + i] = make_uint4(x.x, x.y, y.x, y.y);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const uint2 x = ld8(a + v4 + (uint32_t)(2 * i) * ROWB);
+                const uint2 y = ld8(a + v4 + (uint32_t)(2 * i + 1) * ROWB);
+                buf[4 + i] = make_uint4(x.x, x.y, y.x, y.y);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) buf[i] = ld16(a + (uint32_t)(8 * ph + i) * ROWB);
+            for (int i = 0; i < 8; ++i) buf[i] = ld16(a + (uint32_t)(8 + i) * ROWB);
         }
     };
 
@@ -1024,7 +1022,7 @@ __device__ __forceinline__ void run_piece_g4(const AttnParams& p, const SeqUnits
     // rows.
     auto load_first = [&](uint4* buf, const uint8_t* base, uint32_t voff, int k) {
         const uint32_t va = voff + (k == 0 ? k16 : 0u);
-        const uint32_t vb = voff + (k == 0 ? k16 : (k == 1 ? k4 - 4u * ROWB : 0u));
+        const uint32_t vb = voff + (k == 0 ? k16 : (k == 1 ? k4 : 0u));
         const uint32_t r6 = (k == 1 ? 8u : 6u) * ROWB;
 #pragma unroll
         for (int i = 0; i < 4; ++i) buf[i] = ld16(base + va + (uint32_t)i * ROWB);
