@@ -148,7 +148,7 @@ def test_mixed_chunks_exhaustive(d, C, Hq, Hkv, B, T):
     full_check(w, tab, cache, out, k, v, q, w.n, tk, tv)
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,d", [(130, 2, 2, 64), (97, 4, 2, 128)])
+@pytest.mark.parametrize("B,Hq,Hkv,d", [(130, 2, 2, 64), (97, 4, 2, 128), (71, 8, 2, 128)])
 def test_more_than_64_sequences(B, Hq, Hkv, d):
     """Batches past one wavefront of sequences: the attention split then
     scans the sequences 64 at a time to find each range's first stream, and
