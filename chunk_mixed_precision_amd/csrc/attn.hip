@@ -1107,7 +1107,12 @@ __device__ __forceinline__ void run_piece_g4(const AttnParams& p, const SeqUnits
         v = fmaxf(v, dpp<kDppXor2>(v));
         if constexpr (S == 16) {
             v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
-            v = fmaxf(v, __shfl_xor(v, 16));
+            // the other row of the pair: v_permlane16_swap of v with itself
+            // gives each pair of rows its even row's values in the first
+            // result and its odd row's in the second
+            const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                             __builtin_bit_cast(unsigned, v), false, false);
+            v = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
         } else {
             v = fmaxf(v, dpp<0x128>(v));   // row_ror:8, the other row of the pair
         }
