@@ -85,6 +85,19 @@ inline int check_cache_shape(const mkv_cache* c) {
 }
 
 
+// The query heads of a KV head are attended in groups of 4, 2 and 1 (the
+// kernels' shapes): as many groups of 4 as fit, then one of 2, then one of
+// 1.  Each group is one tile + combine launch pair that reads the KV head's
+// cache; with 1, 2 or 4 heads per KV head that is a single pair.  Returns
+// the group count, sizes in hb[] and first heads in off[].
+int attention_head_groups(int g, int* hb, int* off) {
+    int n = 0, h = 0;
+    while (g - h >= 4) { hb[n] = 4; off[n++] = h; h += 4; }
+    if (g - h >= 2) { hb[n] = 2; off[n++] = h; h += 2; }
+    if (g - h >= 1) { hb[n] = 1; off[n++] = h; h += 1; }
+    return n;
+}
+
 // Decode attention: the argument checks shared by both entry points (no
 // launch, no HIP call).  Resolves a tail_stride of 0 to tail_len.
 int attention_args(const void* q_fp16, int Hq, const mkv_cache* cache, const void* tail_k_fp16,
@@ -95,19 +108,24 @@ int attention_args(const void* q_fp16, int Hq, const mkv_cache* cache, const voi
     if (s) return s;
     if (Hq <= 0 || Hq % cache->Hkv != 0) return MKV_ERR_ARG;
     const int g = Hq / cache->Hkv;
-    if (g != 1 && g != 2 && g != 4) return MKV_ERR_UNSUPPORTED;
+    if (g > 64) return MKV_ERR_UNSUPPORTED;
     if ((long)cache->B * Hq > 2147483647L) return MKV_ERR_UNSUPPORTED;
     if (tail_len < 0 || tail_len >= 4096) return MKV_ERR_ARG;
     if (tail_len > 0 && (!tail_k_fp16 || !tail_v_fp16)) return MKV_ERR_ARG;
     if (*tail_stride == 0) *tail_stride = tail_len;
     if (*tail_stride < tail_len) return MKV_ERR_ARG;
-    {   // the work split counts the cost of the whole cache at capacity in 32-bit granules
-        const int gpi = (512 / cache->d) * mkv::attn_heads_per_row(g) / g;   // group blocks per unit
+    // the work split counts the cost of the whole cache at capacity in
+    // 32-bit granules (for each head group shape used)
+    int hb[32], off[32];
+    const int ngroups = attention_head_groups(g, hb, off);
+    for (int i = 0; i < ngroups; ++i) {
+        const int gg = hb[i];
+        const int gpi = (512 / cache->d) * mkv::attn_heads_per_row(gg) / gg;   // group blocks per unit
         const int bits[3] = {16, 4, 2};
         long long gran = 0;
         for (int k = 0; k < 3; ++k) {
             const long long units = ((long long)cache->cap[k] * (cache->C / mkv::kGroup) + gpi - 1) / gpi;
-            gran += units * ((long long)gpi * mkv::group_bytes(bits[k], cache->d) * mkv::attn_cost16(g, k) /
+            gran += units * ((long long)gpi * mkv::group_bytes(bits[k], cache->d) * mkv::attn_cost16(gg, k) /
                              (16 * mkv::kAttnGranule));
         }
         if (gran * cache->B * cache->Hkv > mkv::kAttnMaxGranules) return MKV_ERR_UNSUPPORTED;
@@ -115,8 +133,9 @@ int attention_args(const void* q_fp16, int Hq, const mkv_cache* cache, const voi
     return MKV_OK;
 }
 
-// Decode attention: the two launches (tile kernel, combine) on checked
-// arguments; `workspace` holds the tile partials of this call.
+// Decode attention: the launch pairs (tile kernel, combine), one per head
+// group, on checked arguments; `workspace` holds the tile partials of one
+// pair at a time (the pairs run in stream order).
 int attention_launch(const void* q_fp16, int Hq, const mkv_cache* cache, const void* tail_k_fp16,
                      const void* tail_v_fp16, int tail_len, int tail_stride, float* out, void* workspace,
                      hipStream_t st) {
@@ -136,7 +155,15 @@ int attention_launch(const void* q_fp16, int Hq, const mkv_cache* cache, const v
     ap.tail_stride = tail_stride;
     ap.out = out;
     ap.qscale = (float)(1.4426950408889634 / sqrt((double)cache->d));
-    return hip_status(mkv::launch_attention(ap, cache->d, Hq / cache->Hkv, st));
+    ap.hpk = Hq / cache->Hkv;
+    int hb[32], off[32];
+    const int ngroups = attention_head_groups(ap.hpk, hb, off);
+    for (int i = 0; i < ngroups; ++i) {
+        ap.hoff = off[i];
+        const int s = hip_status(mkv::launch_attention(ap, cache->d, hb[i], st));
+        if (s) return s;
+    }
+    return MKV_OK;
 }
 
 // ---- the no-allocation variant of decode attention ----------------------
@@ -228,7 +255,9 @@ size_t mkv_workspace_bytes(int op, int a, int b, int c, int e, int f, const int*
         const int B = a, Hq = b, Hkv = c, d = e, C = f;
         if (!caps || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (d != 64 && d != 128) || C <= 0 || C % 32) return 0;
         const int G = attn_workgroups(B, Hkv, d, caps, C);
-        return ((size_t)B * Hkv + G) * (Hq / Hkv) * (d + 4) * sizeof(float) + 16;
+        // records of one head group at a time: at most 4 heads
+        const int hb = Hq / Hkv < 4 ? Hq / Hkv : 4;
+        return ((size_t)B * Hkv + G) * hb * (d + 4) * sizeof(float) + 16;
     }
     return 0;
 }

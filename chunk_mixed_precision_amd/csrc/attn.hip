@@ -339,7 +339,7 @@ __device__ __forceinline__ void run_piece(const AttnParams& p, const SeqUnits<D,
     const int G = L % NG, tq = L / NG;
     const int fx = tok_xor(S, L);
     const int bh = b * p.Hkv + h;
-    const int hq0 = h * HB;              // this row's first query head
+    const int hq0 = h * p.hpk + p.hoff;  // this row's first query head
 
     // segment base pointers of this (b, h)
     const size_t gpc = (size_t)(p.C / kGroup);
@@ -1045,7 +1045,8 @@ __device__ __forceinline__ void run_piece_g4(const AttnParams& p, const SeqUnits
     uint32_t qw[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint4 qc = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + h * HB + (j ^ sg)) * D + 8 * L);
+        const uint4 qc =
+            *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + h * p.hpk + p.hoff + (j ^ sg)) * D + 8 * L);
         qw[j][0] = qc.x; qw[j][1] = qc.y; qw[j][2] = qc.z; qw[j][3] = qc.w;
     }
     float qs[4][8];        // q * log2(e)/sqrt(d) in fp32 (INT-b keys), key-state order
@@ -1596,7 +1597,7 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv, h = bh % p.Hkv;
     const int tid = threadIdx.x, tgi = tid % TG, qd = (tid / TG) % QPR, hb = tid / (TG * QPR);
-    const int hq = h * HB + hb;
+    const int hq = h * p.hpk + p.hoff + hb;
     const int nslots = p.B * p.Hkv + p.G;   // records in the workspace (per query head of the group)
     const int wg = max(0, (int)(((long long)bh * p.G) / (p.B * p.Hkv)) - 1);
     float2 sml;
@@ -1631,7 +1632,7 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnParams p) {
         const uint16_t* tk = p.tail_k + (size_t)bh * p.tail_stride * D;
         for (int i = tid; i < HB * p.tail_len; i += NT) {
             const int th = i / p.tail_len, t = i % p.tail_len;
-            const uint16_t* qp = p.q + ((size_t)b * p.Hq + h * HB + th) * D;
+            const uint16_t* qp = p.q + ((size_t)b * p.Hq + h * p.hpk + p.hoff + th) * D;
             float s = 0.f;
             for (int c = 0; c < D; ++c)
                 s = __builtin_fmaf((float)__builtin_bit_cast(_Float16, qp[c]),

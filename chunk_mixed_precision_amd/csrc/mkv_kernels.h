@@ -124,8 +124,10 @@ struct AttnParams {
     int cap[3];
     const int32_t* seg_count;
     int B, Hkv, Hq, C;
+    int hpk;                // query heads per KV head in q and out (Hq / Hkv)
+    int hoff;               // first query head of this launch's group within a KV head's heads
     int G;                  // workgroups launched (the device may use fewer)
-    float* part;            // [B*Hkv + G][g][d+4]: o[d], m (log2 domain), l, 0, 0
+    float* part;            // [B*Hkv + G][HB][d+4]: o[d], m (log2 domain), l, 0, 0
     const uint16_t* tail_k; // [B][Hkv][tail_stride][d] or NULL; tokens 0..tail_len-1 are used
     const uint16_t* tail_v;
     int tail_len;

@@ -261,7 +261,12 @@ int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T,
  *   workspace   at least mkv_workspace_bytes(MKV_OP_ATTENTION, ...) bytes
  *               (tile partials; no initial contents needed).  Calls that
  *               overlap in time need separate workspaces.
- * Limits: d in {64, 128}; Hq/Hkv in {1, 2, 4}; 0 <= tail_len < 4096; the
+ * Query heads per KV head: any Hq/Hkv up to 64.  The kernels attend the
+ * query heads of a KV head in groups of 4, 2 and 1 (as many groups of 4 as
+ * fit, then one of 2, then one of 1), one launch pair per group, each
+ * reading the KV head's cache: with 1, 2 or 4 heads per KV head the cache is
+ * read once, with 8 twice, with 6 (4 + 2) twice, with 3 (2 + 1) twice.
+ * Limits: d in {64, 128}; Hq/Hkv <= 64; 0 <= tail_len < 4096; the
  * pools at capacity within 2^31 work-split granules of 512 bytes (weighted
  * by bitwidth: 0.6 to 1 TiB of packed cache), else MKV_ERR_UNSUPPORTED.
  * A (b, h) with no cached token and tail_len == 0 yields zeros.
@@ -288,7 +293,7 @@ int mkv_mixed_kv_decode_attention(const void* q_fp16, int Hq,
  *   Returns MKV_ERR_SCRATCH, before any launch, when the call would need
  *   more than MKV_NOALLOC_SCRATCH_BYTES of partials, i.e. when
  *   mkv_workspace_bytes(MKV_OP_ATTENTION, ...) exceeds it (for d = 128
- *   about (B*Hkv + 256) * (Hq/Hkv) <= 15800).
+ *   about (B*Hkv + 256) * min(Hq/Hkv, 4) <= 15800).
  *   Every call on one GPU shares that GPU's array, so calls that overlap in
  *   time on one GPU (other streams, other threads) race and must not be
  *   issued; calls on one stream are ordered and safe.  No part of the array

@@ -140,7 +140,8 @@ def test_attention_argument_errors():
     assert attn(q=None) == E.MKV_ERR_ARG
     assert attn(out=0x704) == E.MKV_ERR_ARG
     assert attn(Hq=3) == E.MKV_ERR_ARG                          # not a multiple of Hkv
-    assert attn(Hq=16) == E.MKV_ERR_UNSUPPORTED                 # 8 query heads per KV head
+    assert attn(Hq=16) == E.MKV_ERR_WORKSPACE                   # 8 query heads per KV head: two groups of 4
+    assert attn(Hq=130) == E.MKV_ERR_UNSUPPORTED                # 65 query heads per KV head
     assert attn(cache=_cache(d=256)) == E.MKV_ERR_UNSUPPORTED
     assert attn(tail_len=5) == E.MKV_ERR_ARG                    # tail pointers missing
     assert attn(tail_len=4096, tk=0x800, tv=0x900) == E.MKV_ERR_ARG
@@ -232,7 +233,7 @@ def test_noalloc_attention_argument_errors():
     assert attn_noalloc(q=None) == E.MKV_ERR_ARG
     assert attn_noalloc(out=0x704) == E.MKV_ERR_ARG
     assert attn_noalloc(Hq=3) == E.MKV_ERR_ARG
-    assert attn_noalloc(Hq=16) == E.MKV_ERR_UNSUPPORTED
+    assert attn_noalloc(Hq=130) == E.MKV_ERR_UNSUPPORTED          # 65 query heads per KV head
     assert attn_noalloc(tail_len=5) == E.MKV_ERR_ARG
     assert attn_noalloc(tail_len=5, tk=0x800, tv=0x900, stride=4) == E.MKV_ERR_ARG
     big = _cache()
