@@ -245,10 +245,10 @@ int mkv_quantize_pack_kv(const void* k_fp16, const void* v_fp16, int T,
  * over every cached token of (b, h) (all segments, in any order: attention
  * does not depend on key order) plus the tail_len fp16 tokens of the tail.
  * Cached values are dequantized in registers; accumulation is fp32.  One
- * launch splits the whole cache into equal byte ranges, one per workgroup,
- * whose wavefronts take single-bitwidth work units dynamically; a second
- * launch merges the partials of each (sequence, KV head) with a
- * log-sum-exp combine.  Because units are handed out dynamically, the fp32
+ * launch splits the whole cache into ranges of equal cost (bytes weighted
+ * by each bitwidth's work per byte), one per workgroup, whose wavefronts
+ * take single-bitwidth work units dynamically; a second launch merges the
+ * partials of each (sequence, KV head) with a log-sum-exp combine.  Because units are handed out dynamically, the fp32
  * summation order (not the result beyond rounding) can differ between calls.
  *
  *   q_fp16      [B][Hq][d] fp16
