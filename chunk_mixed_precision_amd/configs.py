@@ -1,8 +1,8 @@
 """Workload shapes and byte accounting for the mixed-precision KV path.
 
 The five workloads mirror the model families the MoQAE and XQuant pages
-evaluate (LLaMA-2 7B / 13B layers, a LLaMA-3-8B-like GQA layer) at the
-shapes given for this build; all tensors are synthetic (see ``synth``).
+evaluate (LLaMA-2 7B / 13B layers, a LLaMA-3-8B-like GQA layer), each
+with its sizes below; all tensors are synthetic (see ``synth``).
 """
 from __future__ import annotations
 
